@@ -1,0 +1,11 @@
+"""The CPU oracle against its pins (format definition, torch's codec, exact arithmetic,
+closed forms, invariants).  Runs without a GPU."""
+
+import pytest
+
+import oracle_pins
+
+
+@pytest.mark.parametrize("pin", oracle_pins.ALL_PINS, ids=lambda f: f.__name__)
+def test_oracle_pin(pin):
+    pin()

@@ -1,0 +1,144 @@
+"""Plant plausible mistakes in the CPU oracle (on the CPU only) and show that the pins catch each.
+
+If a mutant survives every pin, the pins are too weak to trust the oracle.
+"""
+
+import numpy as np
+import pytest
+
+import oracle
+import oracle_pins
+
+E = oracle.e4m3
+Q = oracle.quant
+G = oracle.gemm
+
+_orig_encode = E.encode
+_orig_decode = E.decode
+
+
+def _encode_half_away(values):
+    v = np.asarray(values, dtype=np.float64)
+    neg = np.signbit(v)
+    a = np.abs(v)
+    _, ex = np.frexp(a)
+    e = np.maximum(ex.astype(np.int64) - 1, -6)
+    quantum = np.ldexp(1.0, e - 3)
+    r = np.floor(a / quantum + 0.5) * quantum            # ties away from zero
+    return _orig_encode(np.where(neg, -r, r))
+
+
+def _encode_no_saturation(values):
+    v = np.asarray(values, dtype=np.float64)
+    out = _orig_encode(v)
+    return np.where(np.abs(v) > 448, out | 0x7F, out).astype(np.uint8)
+
+
+def _encode_drops_negative_zero(values):
+    out = _orig_encode(values)
+    return np.where(out == 0x80, 0, out).astype(np.uint8)
+
+
+def _decode_bias8(codes):
+    return _orig_decode(codes) / 2.0
+
+
+def _quant_tok_divisor(div):
+    def f(x):
+        x = np.asarray(x, dtype=np.float32)
+        m, k = x.shape
+        g = x.reshape(m, k // 128, 128)
+        amax = np.max(np.abs(g), axis=2)
+        s = np.where(amax == 0, np.float32(1), amax / np.float32(div)).astype(np.float32)
+        return E.encode((g / s[:, :, None]).astype(np.float32)).reshape(m, k), s
+    return f
+
+
+def _quant_tok_reciprocal(x):
+    x = np.asarray(x, dtype=np.float32)
+    m, k = x.shape
+    g = x.reshape(m, k // 128, 128)
+    amax = np.max(np.abs(g), axis=2)
+    s = np.where(amax == 0, np.float32(1), amax / np.float32(448)).astype(np.float32)
+    r = (np.float32(1) / s).astype(np.float32)
+    return E.encode((g * r[:, :, None]).astype(np.float32)).reshape(m, k), s
+
+
+def _quant_tok_fp64_division(x):
+    x = np.asarray(x, dtype=np.float32)
+    m, k = x.shape
+    g = x.reshape(m, k // 128, 128)
+    amax = np.max(np.abs(g), axis=2)
+    s = np.where(amax == 0, np.float32(1), amax / np.float32(448)).astype(np.float32)
+    return E.encode(g.astype(np.float64) / s[:, :, None].astype(np.float64)).reshape(m, k), s
+
+
+_orig_block = Q.quantize_per_block
+
+
+def _quant_block_whole_panel(w):
+    """amax over the full N panel of each K block instead of 128x128."""
+    w = np.asarray(w, dtype=np.float32)
+    n, k = w.shape
+    q, sb = _orig_block(w)
+    amax = np.max(np.abs(w.reshape(n, k // 128, 128)), axis=(0, 2))
+    s = np.where(amax == 0, 1, amax / np.float32(448)).astype(np.float32)
+    sb = np.broadcast_to(s, sb.shape).copy()
+    q = E.encode((w.reshape(n, k // 128, 128) / s[None, :, None]).astype(np.float32)).reshape(n, k)
+    return q, sb
+
+
+def _gemm_no_sb(qa, sa, qb, sb):
+    return G.dequantize_rows(qa, sa) @ E.decode(qb).T
+
+
+def _gemm_sb_mod(qa, sa, qb, sb):
+    n = qb.shape[0]
+    rows = np.asarray(sb, np.float64)[np.arange(n) % sb.shape[0]]
+    return G.dequantize_rows(qa, sa) @ G.dequantize_rows(qb, rows).T
+
+
+def _gemm_sa_reversed_kb(qa, sa, qb, sb):
+    return G.dequantize_rows(qa, np.asarray(sa)[:, ::-1]) @ G.dequantize_blocks(qb, sb).T
+
+
+_orig_contig = G.gemm_grouped_contiguous
+_orig_masked = G.gemm_grouped_masked
+
+
+def _contig_off_by_one(qa, sa, qb, sb, m_indices):
+    return _orig_contig(qa, sa, qb, sb, (np.asarray(m_indices) + 1) % np.asarray(qb).shape[0])
+
+
+def _masked_no_clamp_computes_all(qa, sa, qb, sb, masked_m):
+    return _orig_masked(qa, sa, qb, sb, np.full(len(masked_m), np.asarray(qa).shape[1]))
+
+
+MUTANTS = {
+    "encode_ties_away": (E, "encode", _encode_half_away),
+    "encode_no_saturation": (E, "encode", _encode_no_saturation),
+    "encode_drops_negative_zero": (E, "encode", _encode_drops_negative_zero),
+    "decode_bias8": (E, "decode", _decode_bias8),
+    "quant_scale_amax_over_240": (Q, "quantize_per_token_group", _quant_tok_divisor(240)),
+    "quant_reciprocal_multiply": (Q, "quantize_per_token_group", _quant_tok_reciprocal),
+    "quant_fp64_division": (Q, "quantize_per_token_group", _quant_tok_fp64_division),
+    "quant_block_whole_panel": (Q, "quantize_per_block", _quant_block_whole_panel),
+    "gemm_drops_weight_scale": (G, "gemm_nt", _gemm_no_sb),
+    "gemm_weight_scale_index_mod": (G, "gemm_nt", _gemm_sb_mod),
+    "gemm_act_scale_kb_reversed": (G, "gemm_nt", _gemm_sa_reversed_kb),
+    "contiguous_expert_off_by_one": (G, "gemm_grouped_contiguous", _contig_off_by_one),
+    "masked_writes_all_rows": (G, "gemm_grouped_masked", _masked_no_clamp_computes_all),
+}
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_mutant_is_caught(name, monkeypatch):
+    module, attr, fn = MUTANTS[name]
+    monkeypatch.setattr(module, attr, fn)
+    caught = []
+    for pin in oracle_pins.ALL_PINS:
+        try:
+            pin()
+        except (AssertionError, ValueError, IndexError):
+            caught.append(pin.__name__)
+    assert caught, f"mutant {name} survived every pin"
