@@ -1,0 +1,242 @@
+"""Python binding of libdg.so, the gfx950 FP8 block-scaled GEMM library.
+
+Argument marshalling only: every step of the path runs in the HIP kernels of
+libdg.so, called through its C ABI (``include/dg.h``).  PyTorch supplies
+device memory and the current stream; nothing here computes.  If the library
+is not built, every call raises - there is no fallback.
+
+Functions carry the C names:
+
+* ``dg_quantize_per_token_group(x)``  -> (q uint8 (M, K), sa float32 (K/128, ld_sa))
+* ``dg_quantize_per_block(w)``        -> (q uint8 like w, sb float32 ([G,] ceil(N/128), K/128))
+* ``dg_gemm_fp8_nt(a, sa, b, sb)``    -> d bf16 (M, N)
+* ``dg_gemm_fp8_grouped_contiguous(a, sa, b, sb, m_indices)``  -> d bf16 (M_total, N)
+* ``dg_gemm_fp8_grouped_masked(a, sa, b, sb, masked_m)``       -> d bf16 (G, M_max, N)
+* utilities ``dg_get_num_cus``, ``dg_set_num_cus``,
+  ``dg_get_m_alignment_for_contiguous_layout``, ``dg_get_scale_ld``,
+  ``dg_gemm_workspace_size``.
+
+Activation scales use the K-group-major layout of the library: ``sa[kb, row]``
+(for the masked form ``sa[g, kb, row]``), row stride ``ld_sa = sa.shape[-1]``.
+"""
+
+import ctypes
+import os
+import threading
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libdg.so")
+
+_lib = None
+_lock = threading.Lock()
+
+_c_int64 = ctypes.c_int64
+_vp = ctypes.c_void_p
+
+_SIGNATURES = {
+    "dg_status_string": (ctypes.c_char_p, [ctypes.c_int]),
+    "dg_last_error_message": (ctypes.c_char_p, []),
+    "dg_quantize_per_token_group": (ctypes.c_int, [_vp, _c_int64, _c_int64, _vp, _vp, _c_int64, _vp]),
+    "dg_quantize_per_block": (ctypes.c_int, [_vp, _c_int64, _c_int64, _c_int64, _vp, _vp, _vp]),
+    "dg_gemm_fp8_nt": (ctypes.c_int, [_vp, _vp, _c_int64, _vp, _vp, _vp, _c_int64, _c_int64, _c_int64,
+                                      _vp, ctypes.c_size_t, _vp]),
+    "dg_gemm_fp8_grouped_contiguous": (ctypes.c_int, [_vp, _vp, _c_int64, _vp, _vp, _vp, _c_int64, _vp,
+                                                      _c_int64, _c_int64, _c_int64, _vp]),
+    "dg_gemm_fp8_grouped_masked": (ctypes.c_int, [_vp, _vp, _c_int64, _vp, _vp, _vp, _vp, _c_int64,
+                                                  _c_int64, _c_int64, _c_int64, _vp, ctypes.c_size_t, _vp]),
+    "dg_get_num_cus": (ctypes.c_int, []),
+    "dg_set_num_cus": (ctypes.c_int, [ctypes.c_int]),
+    "dg_get_m_alignment_for_contiguous_layout": (ctypes.c_int, []),
+    "dg_get_scale_ld": (_c_int64, [_c_int64]),
+    "dg_gemm_workspace_size": (ctypes.c_size_t, [_c_int64, _c_int64, _c_int64, _c_int64]),
+}
+
+
+def lib():
+    """Load libdg.so once (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        with _lock:
+            if _lib is None:
+                if not os.path.exists(LIB_PATH):
+                    raise RuntimeError(f"libdg.so is not built ({LIB_PATH}); run "
+                                       "`python -m fp8_block_scaled_gemm_amd._build` first")
+                handle = ctypes.CDLL(LIB_PATH)
+                for name, (res, args) in _SIGNATURES.items():
+                    fn = getattr(handle, name)
+                    fn.restype = res
+                    fn.argtypes = args
+                _lib = handle
+    return _lib
+
+
+class DGError(RuntimeError):
+    def __init__(self, fn, status):
+        L = lib()
+        super().__init__(f"{fn}: {L.dg_status_string(status).decode()} "
+                         f"({L.dg_last_error_message().decode()})")
+        self.status = status
+
+
+def _check(fn, status):
+    if status != 0:
+        raise DGError(fn, status)
+
+
+def _stream(t):
+    return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None else None
+
+
+def _bytes(t):
+    """View an FP8 tensor (uint8 or float8_e4m3fn) as uint8."""
+    return t.view(torch.uint8) if t.dtype == torch.float8_e4m3fn else t
+
+
+def _require(cond, msg):
+    if not cond:
+        raise ValueError(msg)
+
+
+def _dev(*ts):
+    for t in ts:
+        _require(t.is_cuda and t.is_contiguous(), "tensors must be contiguous CUDA (HIP) tensors")
+    return ts[0].device
+
+
+# ---------------------------------------------------------------------------
+# utilities
+# ---------------------------------------------------------------------------
+
+def dg_get_num_cus():
+    r = lib().dg_get_num_cus()
+    _check("dg_get_num_cus", r if r < 0 else 0)
+    return r
+
+
+def dg_set_num_cus(n):
+    _check("dg_set_num_cus", lib().dg_set_num_cus(int(n)))
+
+
+def dg_get_m_alignment_for_contiguous_layout():
+    return lib().dg_get_m_alignment_for_contiguous_layout()
+
+
+def dg_get_scale_ld(rows):
+    return lib().dg_get_scale_ld(int(rows))
+
+
+def dg_gemm_workspace_size(m, n, k, num_groups=1):
+    return lib().dg_gemm_workspace_size(int(m), int(n), int(k), int(num_groups))
+
+
+_ws_cache = {}
+
+
+def default_workspace(device, nbytes):
+    """A zero-filled workspace per device, grown on demand (the kernels leave it zeroed)."""
+    key = torch.device(device).index
+    ws = _ws_cache.get(key)
+    if nbytes == 0:
+        return None
+    if ws is None or ws.numel() < nbytes:
+        ws = torch.zeros(max(nbytes, 1 << 20), dtype=torch.uint8, device=device)
+        _ws_cache[key] = ws
+    return ws
+
+
+# ---------------------------------------------------------------------------
+# quantizers
+# ---------------------------------------------------------------------------
+
+def dg_quantize_per_token_group(x, q=None, sa=None):
+    """x float32 (M, K) -> (q uint8 (M, K), sa float32 (K/128, ld_sa)) on x's stream."""
+    _require(x.dtype == torch.float32 and x.dim() == 2, "x must be float32 (M, K)")
+    m, k = x.shape
+    kb = k // 128 if k % 128 == 0 else 0
+    if q is None:
+        q = torch.empty((m, k), dtype=torch.uint8, device=x.device)
+    if sa is None:
+        sa = torch.empty((max(kb, 1), dg_get_scale_ld(m)), dtype=torch.float32, device=x.device)
+    q = _bytes(q)
+    _dev(x, q, sa)
+    _check("dg_quantize_per_token_group",
+           lib().dg_quantize_per_token_group(_ptr(x), m, k, _ptr(q), _ptr(sa), sa.shape[-1], _stream(x)))
+    return q, sa
+
+
+def dg_quantize_per_block(w, q=None, sb=None):
+    """w float32 (N, K) or (G, N, K) -> (q uint8, sb float32 ([G,] ceil(N/128), K/128))."""
+    _require(w.dtype == torch.float32 and w.dim() in (2, 3), "w must be float32 (N, K) or (G, N, K)")
+    grouped = w.dim() == 3
+    g, n, k = (w.shape if grouped else (1,) + tuple(w.shape))
+    nb, kb = -(-n // 128), max(k // 128, 1)
+    if q is None:
+        q = torch.empty(w.shape, dtype=torch.uint8, device=w.device)
+    if sb is None:
+        sb = torch.empty(((g,) if grouped else ()) + (nb, kb), dtype=torch.float32, device=w.device)
+    q = _bytes(q)
+    _dev(w, q, sb)
+    _check("dg_quantize_per_block",
+           lib().dg_quantize_per_block(_ptr(w), g, n, k, _ptr(q), _ptr(sb), _stream(w)))
+    return q, sb
+
+
+# ---------------------------------------------------------------------------
+# GEMMs
+# ---------------------------------------------------------------------------
+
+def dg_gemm_fp8_nt(a, sa, b, sb, d=None, workspace=None, use_workspace=True):
+    """D (M, N) bf16 = A (M, K) * B (N, K)^T with fine-grained scales and promoted accumulation."""
+    a, b = _bytes(a), _bytes(b)
+    m, k = a.shape
+    n = b.shape[0]
+    if d is None:
+        d = torch.empty((m, n), dtype=torch.bfloat16, device=a.device)
+    _dev(a, sa, b, sb, d)
+    if workspace is None and use_workspace:
+        workspace = default_workspace(a.device, dg_gemm_workspace_size(m, n, k, 1))
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check("dg_gemm_fp8_nt",
+           lib().dg_gemm_fp8_nt(_ptr(a), _ptr(sa), sa.shape[-1], _ptr(b), _ptr(sb), _ptr(d), m, n, k,
+                                _ptr(workspace), ws_bytes, _stream(a)))
+    return d
+
+
+def dg_gemm_fp8_grouped_contiguous(a, sa, b, sb, m_indices, d=None):
+    """D (M_total, N): row r uses expert m_indices[r] of B (G, N, K)."""
+    a, b = _bytes(a), _bytes(b)
+    m, k = a.shape
+    g, n, _ = b.shape
+    if d is None:
+        d = torch.empty((m, n), dtype=torch.bfloat16, device=a.device)
+    _require(m_indices.dtype == torch.int32, "m_indices must be int32")
+    _dev(a, sa, b, sb, m_indices, d)
+    _check("dg_gemm_fp8_grouped_contiguous",
+           lib().dg_gemm_fp8_grouped_contiguous(_ptr(a), _ptr(sa), sa.shape[-1], _ptr(b), _ptr(sb),
+                                                _ptr(m_indices), g, _ptr(d), m, n, k, _stream(a)))
+    return d
+
+
+def dg_gemm_fp8_grouped_masked(a, sa, b, sb, masked_m, d=None, workspace=None, use_workspace=True):
+    """D (G, M_max, N): expert g computes only its first masked_m[g] rows; the rest stay untouched."""
+    a, b = _bytes(a), _bytes(b)
+    g, m_max, k = a.shape
+    n = b.shape[1]
+    if d is None:
+        d = torch.empty((g, m_max, n), dtype=torch.bfloat16, device=a.device)
+    _require(masked_m.dtype == torch.int32, "masked_m must be int32")
+    _dev(a, sa, b, sb, masked_m, d)
+    if workspace is None and use_workspace:
+        workspace = default_workspace(a.device, dg_gemm_workspace_size(m_max, n, k, g))
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check("dg_gemm_fp8_grouped_masked",
+           lib().dg_gemm_fp8_grouped_masked(_ptr(a), _ptr(sa), sa.shape[-1], _ptr(b), _ptr(sb), _ptr(d),
+                                            _ptr(masked_m), g, m_max, n, k, _ptr(workspace), ws_bytes,
+                                            _stream(a)))
+    return d

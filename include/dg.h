@@ -1,0 +1,187 @@
+/*
+ * dg.h - C ABI of the MI355X (gfx950) FP8 block-scaled GEMM library (libdg.so).
+ *
+ * The method: FP8 (E4M3) matrix multiplication with DeepSeek-V3 style
+ * fine-grained scaling and two-level (promoted) FP32 accumulation, in three
+ * forms - a normal GEMM, a contiguous-grouped MoE GEMM and a masked-grouped
+ * MoE GEMM.  Sources (DeepGEMM news/blog pages):
+ *   - 机器之心 DeepGEMM report, opening section: fine-grained scaling as in
+ *     DeepSeek-V3; normal and MoE grouped GEMMs; two-level accumulation on
+ *     the general-purpose cores because FP8 tensor-core accumulation is
+ *     imprecise.  Same report, "quick start": the three GEMM forms.
+ *   - ai.abqq.net summary, section 3 "core functions and features": E4M3
+ *     data (4-bit exponent, 3-bit mantissa); contiguous and masked layouts.
+ *   - 3loumao explainer, section 03 "how DeepSeek innovated": the contiguous
+ *     layout joins every expert's rows into one block; the masked layout marks
+ *     which rows to compute and skips the rest at run time.
+ *   - CSDN "DeepGEMM: concise, efficient ..." article, "utilities": maximum
+ *     number of compute units used, the contiguous-layout alignment, and the
+ *     aligned column-major activation-scale tensor.
+ *
+ * Conventions shared by every entry point:
+ *   - All data pointers are DEVICE pointers owned by the caller; the library
+ *     keeps none of them after it returns.  All pointers must be 16-byte
+ *     aligned.
+ *   - E4M3 means the OCP E4M3FN encoding (largest finite value 448).  FP8
+ *     operands are passed as uint8_t bytes; bf16 outputs as uint16_t bits.
+ *   - K (the reduction length) must be a positive multiple of 128.
+ *   - Activation scales `sa` are stored K-group-major ("MN-major"):
+ *     sa[kb * ld_sa + row] is the scale of row `row`, columns
+ *     [128*kb, 128*kb+128).  ld_sa >= rows and ld_sa % 4 == 0
+ *     (dg_get_scale_ld gives the smallest such value).
+ *   - Weight scales `sb` are stored block-row-major: sb[nb * (k/128) + kb]
+ *     is the scale of rows [128*nb, 128*nb+128) (a partial last block is
+ *     allowed), columns [128*kb, 128*kb+128).
+ *   - Work is enqueued on `stream` (a hipStream_t; NULL = the default
+ *     stream) without any host synchronisation: device-resident counts
+ *     (m_indices, masked_m) are read by the kernels only.
+ *   - Return value: DG_OK, or a negative dg_status.  Argument errors are
+ *     detected synchronously, before anything is launched.  A failed launch
+ *     returns DG_ERR_HIP.  Faults inside a kernel surface at the caller's next
+ *     synchronisation.  A zero-sized problem (m == 0, num_groups == 0) is a
+ *     successful no-op.  No C++ exception crosses this interface.
+ *   - Entry points are reentrant; dg_set_num_cus is process-wide.
+ */
+#ifndef DG_H_
+#define DG_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef void* dg_stream_t; /* hipStream_t */
+
+enum dg_status {
+  DG_OK = 0,
+  DG_ERR_INVALID_ARG = -1, /* a pointer, size, stride or alignment is invalid */
+  DG_ERR_UNSUPPORTED = -2, /* valid but outside what the kernels implement */
+  DG_ERR_WORKSPACE = -3,   /* reserved: workspace too small is not an error (split-K is skipped) */
+  DG_ERR_HIP = -4          /* a HIP runtime call failed */
+};
+
+/* Human-readable name of a status code (static string). */
+const char* dg_status_string(int status);
+
+/* Detail of the last non-OK return on the calling thread (thread-local, static storage). */
+const char* dg_last_error_message(void);
+
+/*
+ * Per-token-group activation quantizer (1 x 128).
+ * Fine-grained scaling as in DeepSeek-V3 (机器之心 report, opening section),
+ * E4M3 data (ai.abqq.net summary, section 3).  For each row r and K group kb:
+ *   amax = max |x[r, 128kb .. 128kb+127]|
+ *   s    = amax / 448 (IEEE fp32 division; s = 1 when amax == 0)
+ *   q    = E4M3 round-to-nearest-even, saturating, of fl32(x / s) (IEEE division)
+ * x  : fp32 (m, k) row-major, read only.
+ * q  : E4M3 bytes (m, k) row-major, written.
+ * sa : fp32 scales, written at sa[kb * ld_sa + r] for r < m; entries r >= m untouched.
+ * Errors: DG_ERR_INVALID_ARG for null/misaligned pointers, m < 0, k % 128 != 0,
+ * ld_sa < m or ld_sa % 4 != 0.  Output is bit-exact (the result is unique).
+ */
+int dg_quantize_per_token_group(const float* x, int64_t m, int64_t k, uint8_t* q, float* sa,
+                                int64_t ld_sa, dg_stream_t stream);
+
+/*
+ * Per-block weight quantizer (128 x 128), for num_groups stacked (n, k) matrices.
+ * Same rule as above with the amax over each 128 x 128 block (a partial last
+ * block at the N edge takes its amax over the rows present).
+ * w  : fp32 (num_groups, n, k) row-major, read only.
+ * q  : E4M3 bytes (num_groups, n, k), written.
+ * sb : fp32 (num_groups, ceil(n/128), k/128), written.
+ * Errors: DG_ERR_INVALID_ARG for null/misaligned pointers, n < 0, num_groups < 0,
+ * k % 128 != 0.  Output is bit-exact.
+ */
+int dg_quantize_per_block(const float* w, int64_t num_groups, int64_t n, int64_t k, uint8_t* q,
+                          float* sb, dg_stream_t stream);
+
+/*
+ * Normal FP8 GEMM  D = A * B^T  with two-level accumulation (机器之心 report,
+ * opening section and "quick start"; 3loumao explainer, section 03).
+ * After every 128-deep K block the MFMA partial P is promoted into FP32
+ * accumulators:  acc += P * fl32(sa[row, kb] * sb[n/128, kb]);  D = bf16_rne(acc).
+ * a  : E4M3 (m, k) row-major.        sa : fp32, MN-major with stride ld_sa (see above).
+ * b  : E4M3 (n, k) row-major.        sb : fp32 (ceil(n/128), k/128).
+ * d  : bf16 (m, n) row-major, written.
+ * workspace : optional device scratch for split-K on small-m shapes; it must be
+ *   zero-filled before its first use and is left zero-filled in its counter
+ *   area after each call; calls sharing one workspace must be ordered on one
+ *   stream.  NULL or too small (see dg_gemm_workspace_size) => no split-K:
+ *   still correct, slower for small m.
+ * Errors: DG_ERR_INVALID_ARG for null/misaligned pointers, negative sizes,
+ * k % 128 != 0, ld_sa < m or ld_sa % 4 != 0.  Deterministic: the same inputs
+ * give bit-identical outputs.
+ */
+int dg_gemm_fp8_nt(const uint8_t* a, const float* sa, int64_t ld_sa, const uint8_t* b,
+                   const float* sb, uint16_t* d, int64_t m, int64_t n, int64_t k, void* workspace,
+                   size_t workspace_bytes, dg_stream_t stream);
+
+/*
+ * Contiguous-grouped MoE GEMM (3loumao explainer, section 03: every expert's
+ * rows joined into one block; ai.abqq.net summary, section 3).
+ * Rows of A are grouped in blocks of dg_get_m_alignment_for_contiguous_layout()
+ * (128) rows; every row of one block carries the same expert index
+ * m_indices[row] in [0, num_groups).  Row r of D is A[r] * B[m_indices[r]]^T.
+ * A block whose index is outside [0, num_groups) (e.g. -1 padding) is skipped
+ * and its D rows are left unwritten.
+ * a  : E4M3 (m_total, k);  sa : fp32 MN-major, stride ld_sa >= m_total.
+ * b  : E4M3 (num_groups, n, k);  sb : fp32 (num_groups, ceil(n/128), k/128).
+ * m_indices : int32 (m_total,), DEVICE memory, read by the kernel only.
+ * d  : bf16 (m_total, n).
+ * Errors: as dg_gemm_fp8_nt, plus m_total % 128 != 0.
+ */
+int dg_gemm_fp8_grouped_contiguous(const uint8_t* a, const float* sa, int64_t ld_sa,
+                                   const uint8_t* b, const float* sb, const int32_t* m_indices,
+                                   int64_t num_groups, uint16_t* d, int64_t m_total, int64_t n,
+                                   int64_t k, dg_stream_t stream);
+
+/*
+ * Masked-grouped MoE GEMM (3loumao explainer, section 03: mark which rows to
+ * compute and skip invalid work such as empty decode tokens at run time).
+ * For expert g only rows r < min(max(masked_m[g], 0), m_max) are computed and
+ * written; rows at or past that count are never written.
+ * a  : E4M3 (num_groups, m_max, k);  sa : fp32 (num_groups, k/128, ld_sa), ld_sa >= m_max.
+ * b  : E4M3 (num_groups, n, k);      sb : fp32 (num_groups, ceil(n/128), k/128).
+ * d  : bf16 (num_groups, m_max, n).
+ * masked_m : int32 (num_groups,), DEVICE memory, read by the kernel only.
+ * workspace : as dg_gemm_fp8_nt (used for split-K when m_max is small).
+ * Errors: as dg_gemm_fp8_nt.
+ */
+int dg_gemm_fp8_grouped_masked(const uint8_t* a, const float* sa, int64_t ld_sa,
+                               const uint8_t* b, const float* sb, uint16_t* d,
+                               const int32_t* masked_m, int64_t num_groups, int64_t m_max,
+                               int64_t n, int64_t k, void* workspace, size_t workspace_bytes,
+                               dg_stream_t stream);
+
+/*
+ * Utilities (CSDN article, "utilities": cap on the compute units used,
+ * contiguous-layout alignment, aligned column-major scale tensor).
+ */
+
+/* Current cap on the compute units the persistent GEMM grid uses (default: all
+ * CUs of the current device; queries the device on first use, returns < 0 on a
+ * HIP error). */
+int dg_get_num_cus(void);
+
+/* Set that cap (1 <= n); n larger than the device's CU count is clamped.  Process-wide.
+ * Returns DG_OK or DG_ERR_INVALID_ARG. */
+int dg_set_num_cus(int n);
+
+/* Row alignment required of each group in the contiguous layout: 128. */
+int dg_get_m_alignment_for_contiguous_layout(void);
+
+/* Smallest valid ld_sa for `rows` rows: rows rounded up to a multiple of 4 (16 bytes). */
+int64_t dg_get_scale_ld(int64_t rows);
+
+/* Workspace bytes that let dg_gemm_fp8_nt / dg_gemm_fp8_grouped_masked use
+ * split-K for the given shape (m = rows per group; num_groups = 1 for the
+ * normal GEMM).  0 means split-K is never used for that shape. */
+size_t dg_gemm_workspace_size(int64_t m, int64_t n, int64_t k, int64_t num_groups);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DG_H_ */

