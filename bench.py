@@ -1,0 +1,385 @@
+"""Benchmark of the FP8 block-scaled GEMM hot path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload dense_v3|small|contiguous|masked|
+                     large_dense|zipf] [--no-cpu-baseline] [--cpu-seconds S]
+
+One step is one pass of the whole hot path over one batch of synthetic input:
+weight quantization (128x128 blocks) of every weight matrix of the workload,
+then, per GEMM shape, activation quantization (1x128 groups) followed by the
+FP8 GEMM with promoted accumulation - every kernel of the library, in the order
+a training forward pass runs them.  Inputs are resident in HBM before timing.
+Prints ONE JSON line: the workload's GEMM FP8 TFLOP/s over the whole step, plus
+per-shape GEMM TFLOP/s and HBM GB/s, the roofline of the dominant GEMM kernel
+(timed with HIP events on the launch stream) and the CPU oracle's throughput on
+a bounded sample of the same workload.
+
+Workloads: DeepSeek-V3/R1 inference shapes (prefill and decode, no tensor
+parallelism - the pages' own benchmark set, 机器之心 DeepGEMM report,
+"performance") are not a public dataset; seeded synthetic inputs of those
+shapes stand in for them.
+"""
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "FP8 TFLOPS + HBM GB/s per GEMM shape on 1 MI355X (roofline fraction)"
+PEAK_FP8_TFLOPS = 5000.0      # MI355X dense FP8 MFMA, published
+PEAK_HBM_GBS = 8000.0         # MI355X HBM3E, published
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="dense_v3",
+                    choices=["dense_v3", "small", "contiguous", "masked", "large_dense", "zipf"])
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target CPU work of the oracle sample")
+    return ap.parse_args()
+
+
+# ---------------------------------------------------------------------------
+# GPU-side seeded input generation (same recipe as fp8_block_scaled_gemm_amd.inputs, drawn on the
+# device so that multi-GB workloads are ready in seconds)
+# ---------------------------------------------------------------------------
+
+class Gen:
+    def __init__(self, torch, dev, seed):
+        self.t = torch
+        self.dev = dev
+        self.g = torch.Generator(device=dev)
+        self.g.manual_seed(seed)
+
+    def normal(self, shape, std=1.0):
+        return self.t.randn(shape, generator=self.g, device=self.dev, dtype=self.t.float32) * std
+
+    def activations(self, m, k):
+        a = self.normal((m, k))
+        n_out = max(1, int(round(0.01 * m)))
+        rows = self.t.randperm(m, generator=self.g, device=self.dev)[:n_out]
+        a[rows] *= 100.0
+        return a
+
+
+# ---------------------------------------------------------------------------
+# ops of one step
+# ---------------------------------------------------------------------------
+
+class Op:
+    def __init__(self, kind, label, launch, flops=0.0, nbytes=0.0, config=""):
+        self.kind, self.label, self.launch = kind, label, launch
+        self.flops, self.nbytes, self.config = float(flops), float(nbytes), config
+        self.times = []   # ms per timed step
+
+
+def dense_gemm_bytes(m, n, k):
+    """Algorithmic HBM bytes of one dense GEMM: A + its scales, B + its scales, bf16 D."""
+    return m * k + 4 * m * (k // 128) + n * k + 4 * (-(-n // 128)) * (k // 128) + 2 * m * n
+
+
+def quant_bytes(elems, k):
+    """fp32 read + E4M3 write + one fp32 scale per 128 elements."""
+    return 4 * elems + elems + 4 * elems // 128
+
+
+def build_dense(torch, dg, dev, shapes, name):
+    """Ops for a list of dense (M, N, K) shapes sharing weights per (N, K)."""
+    gen = Gen(torch, dev, 1234)
+    ops = []
+    weights = {}
+    for (m, n, k) in shapes:
+        if (n, k) not in weights:
+            w32 = gen.normal((n, k), 0.02)
+            qb = torch.empty((n, k), dtype=torch.uint8, device=dev)
+            sb = torch.empty((-(-n // 128), k // 128), dtype=torch.float32, device=dev)
+            weights[(n, k)] = (w32, qb, sb)
+            ops.append(Op("wquant", f"wq {n}x{k}",
+                          (lambda w32=w32, qb=qb, sb=sb: dg.dg_quantize_per_block(w32, q=qb, sb=sb)),
+                          nbytes=quant_bytes(n * k, k)))
+    for (m, n, k) in shapes:
+        w32, qb, sb = weights[(n, k)]
+        a32 = gen.activations(m, k)
+        qa = torch.empty((m, k), dtype=torch.uint8, device=dev)
+        sa = torch.empty((k // 128, dg.dg_get_scale_ld(m)), dtype=torch.float32, device=dev)
+        d = torch.empty((m, n), dtype=torch.bfloat16, device=dev)
+        ws = dg.default_workspace(dev, dg.dg_gemm_workspace_size(m, n, k, 1))
+        ops.append(Op("aquant", f"aq {m}x{k}",
+                      (lambda a32=a32, qa=qa, sa=sa: dg.dg_quantize_per_token_group(a32, q=qa, sa=sa)),
+                      nbytes=quant_bytes(m * k, k)))
+        ops.append(Op("gemm", f"{m}x{n}x{k}",
+                      (lambda qa=qa, sa=sa, qb=qb, sb=sb, d=d, ws=ws: dg.dg_gemm_fp8_nt(qa, sa, qb, sb, d=d,
+                                                                                         workspace=ws)),
+                      flops=2.0 * m * n * k, nbytes=dense_gemm_bytes(m, n, k),
+                      config=dg.dg_gemm_config_name(0, m, n, k, 1)))
+    return ops
+
+
+def build_contiguous(torch, dg, dev, cases):
+    """cases: list of (label, sizes (np int array), n, k)."""
+    from fp8_block_scaled_gemm_amd import inputs
+    gen = Gen(torch, dev, 4321)
+    ops = []
+    for label, sizes, n, k in cases:
+        g = len(sizes)
+        m_idx_np, starts, valid_np = inputs.contiguous_layout(sizes)
+        m_total = m_idx_np.shape[0]
+        w32 = gen.normal((g, n, k), 0.02)
+        qb = torch.empty((g, n, k), dtype=torch.uint8, device=dev)
+        sb = torch.empty((g, -(-n // 128), k // 128), dtype=torch.float32, device=dev)
+        a32 = gen.activations(m_total, k) * torch.from_numpy(valid_np).to(dev).float()[:, None]
+        qa = torch.empty((m_total, k), dtype=torch.uint8, device=dev)
+        sa = torch.empty((k // 128, dg.dg_get_scale_ld(m_total)), dtype=torch.float32, device=dev)
+        d = torch.empty((m_total, n), dtype=torch.bfloat16, device=dev)
+        m_idx = torch.from_numpy(m_idx_np).to(dev)
+        rows = int(np.sum(sizes))
+        ops.append(Op("wquant", f"wq {g}x{n}x{k}",
+                      (lambda w32=w32, qb=qb, sb=sb: dg.dg_quantize_per_block(w32, q=qb, sb=sb)),
+                      nbytes=quant_bytes(g * n * k, k)))
+        ops.append(Op("aquant", f"aq {m_total}x{k}",
+                      (lambda a32=a32, qa=qa, sa=sa: dg.dg_quantize_per_token_group(a32, q=qa, sa=sa)),
+                      nbytes=quant_bytes(m_total * k, k)))
+        nbytes = (m_total * k + 4 * m_total * (k // 128) + g * (n * k + 4 * (-(-n // 128)) * (k // 128))
+                  + 2 * m_total * n + 4 * m_total)
+        ops.append(Op("gemm", f"{label} G={g} rows={rows} (padded {m_total}) N={n} K={k}",
+                      (lambda qa=qa, sa=sa, qb=qb, sb=sb, m_idx=m_idx, d=d:
+                       dg.dg_gemm_fp8_grouped_contiguous(qa, sa, qb, sb, m_idx, d=d)),
+                      flops=2.0 * rows * n * k, nbytes=nbytes,
+                      config=dg.dg_gemm_config_name(1, m_total, n, k, g)))
+    return ops
+
+
+def build_masked(torch, dg, dev, cases):
+    """cases: list of (masked_m np int32 array, m_max, n, k)."""
+    gen = Gen(torch, dev, 999)
+    ops = []
+    for masked_np, m_max, n, k in cases:
+        g = len(masked_np)
+        w32 = gen.normal((g, n, k), 0.02)
+        qb = torch.empty((g, n, k), dtype=torch.uint8, device=dev)
+        sb = torch.empty((g, -(-n // 128), k // 128), dtype=torch.float32, device=dev)
+        a32 = gen.activations(g * m_max, k).reshape(g, m_max, k)
+        qa = torch.empty((g, m_max, k), dtype=torch.uint8, device=dev)
+        sa = torch.empty((g, k // 128, dg.dg_get_scale_ld(m_max)), dtype=torch.float32, device=dev)
+        d = torch.empty((g, m_max, n), dtype=torch.bfloat16, device=dev)
+        masked = torch.from_numpy(masked_np.astype(np.int32)).to(dev)
+        ws = dg.default_workspace(dev, dg.dg_gemm_workspace_size(m_max, n, k, g))
+        rows = int(np.sum(np.clip(masked_np, 0, m_max)))
+        active = int(np.sum(masked_np > 0))
+        ops.append(Op("wquant", f"wq {g}x{n}x{k}",
+                      (lambda w32=w32, qb=qb, sb=sb: dg.dg_quantize_per_block(w32, q=qb, sb=sb)),
+                      nbytes=quant_bytes(g * n * k, k)))
+        ops.append(Op("aquant", f"aq {g}x{m_max}x{k}",
+                      (lambda a32=a32, qa=qa, sa=sa: dg.dg_quantize_per_token_group(a32, q=qa, sa=sa)),
+                      nbytes=quant_bytes(g * m_max * k, k)))
+        nbytes = active * (n * k + 4 * (-(-n // 128)) * (k // 128)) + rows * (k + k // 32 + 2 * n) + 4 * g
+        ops.append(Op("gemm", f"masked G={g} rows={rows} M_max={m_max} N={n} K={k}",
+                      (lambda qa=qa, sa=sa, qb=qb, sb=sb, d=d, masked=masked, ws=ws:
+                       dg.dg_gemm_fp8_grouped_masked(qa, sa, qb, sb, masked, d=d, workspace=ws)),
+                      flops=2.0 * rows * n * k, nbytes=nbytes,
+                      config=dg.dg_gemm_config_name(2, m_max, n, k, g)))
+    return ops
+
+
+def build_workload(name, torch, dg, dev):
+    from fp8_block_scaled_gemm_amd import inputs
+    if name == "dense_v3":
+        # decode shapes first, then prefill, then the second decode size: the weights read by the two
+        # decode passes are separated by > 1 GB of traffic, so neither pass is served by the 256 MB MALL
+        order = [64, 4096, 128]
+        shapes = [(m, n, k) for m in order for (n, k) in inputs.DENSE_V3_NK]
+        desc = ("DeepSeek-V3 dense GEMMs: M in {64,128,4096} x (N,K) in {(2112,7168),(24576,1536),"
+                "(32768,512),(7168,16384),(4096,7168),(7168,2048)}; A~N(0,1) with 1% rows x100, B~N(0,0.02^2)")
+        return build_dense(torch, dg, dev, shapes, name), desc
+    if name == "small":
+        return build_dense(torch, dg, dev, [(128, 512, 512)], name), "M=128, N=512, K=512"
+    if name == "large_dense":
+        return build_dense(torch, dg, dev, [(16384, 7168, 16384)], name), "dense prefill M=16384, N=7168, K=16384"
+    if name == "contiguous":
+        cases = []
+        for g in (4, 8):
+            sizes = inputs.uniform_group_sizes(inputs.rng_for("contiguous", g), g)
+            for (n, k) in inputs.GROUPED_NK:
+                cases.append(("contiguous", sizes, n, k))
+        return (build_contiguous(torch, dg, dev, cases),
+                "contiguous-grouped MoE: G in {4,8}, ~8192 rows/expert (+-25%) padded to 128, (N,K) in "
+                "{(4096,7168),(7168,2048)}")
+    if name == "zipf":
+        sizes = inputs.zipf_group_sizes(inputs.rng_for("zipf"))
+        return (build_contiguous(torch, dg, dev, [("zipf", sizes, 2048, 7168)]),
+                "contiguous-grouped MoE: G=64, 32768 routed rows, Zipf(1.1) sizes padded to 128, N=2048, K=7168")
+    if name == "masked":
+        masked = inputs.masked_counts(inputs.rng_for("masked"))
+        cases = [(masked, 256, n, k) for (n, k) in inputs.GROUPED_NK]
+        return (build_masked(torch, dg, dev, cases),
+                "masked-grouped MoE decode: G=32, 256-row buffers, masked_m ~ U{0..256}, (N,K) in "
+                "{(4096,7168),(7168,2048)}")
+    raise ValueError(name)
+
+
+# ---------------------------------------------------------------------------
+# CPU oracle baseline on a bounded sample
+# ---------------------------------------------------------------------------
+
+def cpu_baseline(workload, seconds):
+    import oracle
+    from fp8_block_scaled_gemm_amd import inputs
+    try:
+        from threadpoolctl import threadpool_info
+        blas_threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        blas_threads = 1
+    # sample: for each (N, K) of the dense V3 set, 64 activation rows x `rows_b` weight rows through
+    # the whole oracle path (quantize A rows, quantize B rows, fp64 GEMM); rows_b scaled to the budget
+    nk = inputs.DENSE_V3_NK if workload == "dense_v3" else [(512, 512)]
+    rng = inputs.rng_for("cpu_sample")
+
+    def run(rows_b):
+        flops, t = 0.0, 0.0
+        for (n, k) in nk:
+            a = inputs.activations_with_outliers(rng, 64, k)
+            b = inputs.normal(rng, (min(rows_b, n), k), 0.02)
+            t0 = time.perf_counter()
+            qa, sa = oracle.quant.quantize_per_token_group(a)
+            qb, sb = oracle.quant.quantize_per_block(b)
+            oracle.gemm.gemm_nt(qa, sa, qb, sb)
+            t += time.perf_counter() - t0
+            flops += 2.0 * 64 * b.shape[0] * k
+        return flops, t
+
+    f0, t0 = run(128)                     # calibration
+    rows_b = int(max(128, min(8192, 128 * seconds / max(t0, 1e-3))) // 128 * 128)
+    f, t = run(rows_b)
+    return {"value": f / t / 1e12, "unit": "TFLOP/s", "cores": int(blas_threads), "kind": "oracle",
+            "sample": (f"oracle quantize + fp64 GEMM of 64 activation rows x {rows_b} weight rows for each (N,K) "
+                       f"of the workload ({f / 1e9:.2f} GFLOP in {t:.1f} s; quantization single-threaded numpy, "
+                       f"GEMM on {blas_threads} BLAS threads)"),
+            "seconds": t}
+
+
+# ---------------------------------------------------------------------------
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py: this build measures one GPU only (got --gpus {args.gpus}); the path has no "
+              "multi-GPU mode - see the sharding notes of the design document", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import fp8_block_scaled_gemm_amd as dg
+
+    if not torch.cuda.is_available():
+        print("bench.py: no GPU visible", file=sys.stderr)
+        sys.exit(1)
+    dev = torch.device("cuda", 0)
+    dg.lib()
+    ops, desc = build_workload(args.workload, torch, dg, dev)
+    torch.cuda.synchronize()
+    print(f"[bench] workload {args.workload}: {len(ops)} ops per step", file=sys.stderr, flush=True)
+
+    n = len(ops)
+
+    def step(record):
+        if record:
+            ev = [torch.cuda.Event(enable_timing=True) for _ in range(2 * n)]
+            for i, op in enumerate(ops):
+                ev[2 * i].record()
+                op.launch()
+                ev[2 * i + 1].record()
+            return ev
+        for op in ops:
+            op.launch()
+        return None
+
+    for _ in range(args.warmup):
+        step(False)
+    torch.cuda.synchronize()
+    print("[bench] warmup done", file=sys.stderr, flush=True)
+
+    all_ev = []
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        all_ev.append(step(True))
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_per_step = (t1 - t0) * 1e3 / args.steps
+    for ev in all_ev:
+        for i, op in enumerate(ops):
+            op.times.append(ev[2 * i].elapsed_time(ev[2 * i + 1]))
+    print(f"[bench] timed {args.steps} steps: {ms_per_step:.3f} ms/step", file=sys.stderr, flush=True)
+
+    gemm_flops = sum(op.flops for op in ops if op.kind == "gemm")
+    value = gemm_flops / (ms_per_step * 1e-3) / 1e12
+
+    shapes = []
+    for op in ops:
+        if op.kind != "gemm":
+            continue
+        t = float(np.median(op.times)) * 1e-3
+        tf = op.flops / t / 1e12
+        gb = op.nbytes / t / 1e9
+        shapes.append({"shape": op.label, "config": op.config, "us": round(t * 1e6, 2),
+                       "tflops": round(tf, 1), "gbps": round(gb, 1),
+                       "mfma_frac": round(tf / PEAK_FP8_TFLOPS, 4), "hbm_frac": round(gb / PEAK_HBM_GBS, 4),
+                       "roofline_frac": round(max(op.flops / (PEAK_FP8_TFLOPS * 1e12),
+                                                  op.nbytes / (PEAK_HBM_GBS * 1e9)) / t, 4)})
+
+    # dominant GEMM kernel: the kernel instance (tile configuration; the K split is a launch
+    # parameter of the same kernel) with the most event time over the timed region
+    by_cfg = {}
+    for op in ops:
+        if op.kind == "gemm":
+            by_cfg.setdefault(op.config.split("/split")[0], []).append(op)
+    dom_cfg, dom_ops = max(by_cfg.items(), key=lambda kv: sum(sum(o.times) for o in kv[1]))
+    tot_t = sum(sum(o.times) for o in dom_ops) * 1e-3
+    launches = sum(len(o.times) for o in dom_ops)
+    tot_f = sum(o.flops * len(o.times) for o in dom_ops)
+    tot_b = sum(o.nbytes * len(o.times) for o in dom_ops)
+    mfma_bound = tot_f / (PEAK_FP8_TFLOPS * 1e12) >= tot_b / (PEAK_HBM_GBS * 1e9)
+    if mfma_bound:
+        achieved, peak, unit = tot_f / tot_t / 1e12, PEAK_FP8_TFLOPS, "TFLOP/s"
+    else:
+        achieved, peak, unit = tot_b / tot_t / 1e9, PEAK_HBM_GBS, "GB/s"
+    roofline = {"bound": "mfma" if mfma_bound else "hbm", "achieved": round(achieved, 1), "peak": peak,
+                "unit": unit, "frac": round(achieved / peak, 4), "traffic": None,
+                "kernel": f"gemm_fp8_kernel {dom_cfg}", "launches": launches,
+                "avg_launch_us": round(tot_t / launches * 1e6, 2),
+                "shapes": sorted({o.label for o in dom_ops})}
+
+    quant = {}
+    for kind in ("wquant", "aquant"):
+        ks = [op for op in ops if op.kind == kind]
+        if ks:
+            t = sum(float(np.median(o.times)) for o in ks) * 1e-3
+            b = sum(o.nbytes for o in ks)
+            quant[kind] = {"us": round(t * 1e6, 1), "gbps": round(b / t / 1e9, 1),
+                           "hbm_frac": round(b / t / 1e9 / PEAK_HBM_GBS, 4)}
+    gemm_only_ms = sum(float(np.median(o.times)) for o in ops if o.kind == "gemm")
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        print("[bench] cpu baseline ...", file=sys.stderr, flush=True)
+        cpu = cpu_baseline(args.workload, args.cpu_seconds)
+
+    out = {"metric": METRIC, "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+           "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4), "higher_is_better": True,
+           "scaling": "weak", "vs_baseline": None, "dtype": "fp8_e4m3", "data": "synthetic",
+           "config": {"workload": args.workload, "description": desc, "gemms": len(shapes),
+                      "step": "weight quantization (all weights) + per shape: activation quantization, FP8 GEMM",
+                      "gemm_only_tflops": round(gemm_flops / (gemm_only_ms * 1e-3) / 1e12, 1),
+                      "gemm_only_ms": round(gemm_only_ms, 4)},
+           "roofline": roofline, "cpu_baseline": cpu, "quant": quant, "shapes": shapes}
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -38,7 +38,7 @@ _vp = ctypes.c_void_p
 _SIGNATURES = {
     "dg_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "dg_last_error_message": (ctypes.c_char_p, []),
-    "dg_quantize_per_token_group": (ctypes.c_int, [_vp, _c_int64, _c_int64, _vp, _vp, _c_int64, _vp]),
+    "dg_quantize_per_token_group": (ctypes.c_int, [_vp, _c_int64, _c_int64, _c_int64, _vp, _vp, _c_int64, _vp]),
     "dg_quantize_per_block": (ctypes.c_int, [_vp, _c_int64, _c_int64, _c_int64, _vp, _vp, _vp]),
     "dg_gemm_fp8_nt": (ctypes.c_int, [_vp, _vp, _c_int64, _vp, _vp, _vp, _c_int64, _c_int64, _c_int64,
                                       _vp, ctypes.c_size_t, _vp]),
@@ -51,6 +51,7 @@ _SIGNATURES = {
     "dg_get_m_alignment_for_contiguous_layout": (ctypes.c_int, []),
     "dg_get_scale_ld": (_c_int64, [_c_int64]),
     "dg_gemm_workspace_size": (ctypes.c_size_t, [_c_int64, _c_int64, _c_int64, _c_int64]),
+    "dg_gemm_config_name": (ctypes.c_char_p, [ctypes.c_int, _c_int64, _c_int64, _c_int64, _c_int64]),
 }
 
 
@@ -135,6 +136,11 @@ def dg_gemm_workspace_size(m, n, k, num_groups=1):
     return lib().dg_gemm_workspace_size(int(m), int(n), int(k), int(num_groups))
 
 
+def dg_gemm_config_name(layout, m, n, k, num_groups=1):
+    """Tile configuration / K split the GEMM picks (layout 0 normal, 1 contiguous, 2 masked)."""
+    return lib().dg_gemm_config_name(int(layout), int(m), int(n), int(k), int(num_groups)).decode()
+
+
 _ws_cache = {}
 
 
@@ -155,18 +161,21 @@ def default_workspace(device, nbytes):
 # ---------------------------------------------------------------------------
 
 def dg_quantize_per_token_group(x, q=None, sa=None):
-    """x float32 (M, K) -> (q uint8 (M, K), sa float32 (K/128, ld_sa)) on x's stream."""
-    _require(x.dtype == torch.float32 and x.dim() == 2, "x must be float32 (M, K)")
-    m, k = x.shape
+    """x float32 (M, K) -> (q uint8 (M, K), sa float32 (K/128, ld_sa)); or x (G, M, K) ->
+    (q (G, M, K), sa (G, K/128, ld_sa)) for the per-expert masked layout.  Runs on x's stream."""
+    _require(x.dtype == torch.float32 and x.dim() in (2, 3), "x must be float32 (M, K) or (G, M, K)")
+    grouped = x.dim() == 3
+    g, m, k = (x.shape if grouped else (1,) + tuple(x.shape))
     kb = k // 128 if k % 128 == 0 else 0
     if q is None:
-        q = torch.empty((m, k), dtype=torch.uint8, device=x.device)
+        q = torch.empty(x.shape, dtype=torch.uint8, device=x.device)
     if sa is None:
-        sa = torch.empty((max(kb, 1), dg_get_scale_ld(m)), dtype=torch.float32, device=x.device)
+        sa = torch.empty(((g,) if grouped else ()) + (max(kb, 1), dg_get_scale_ld(m)),
+                         dtype=torch.float32, device=x.device)
     q = _bytes(q)
     _dev(x, q, sa)
     _check("dg_quantize_per_token_group",
-           lib().dg_quantize_per_token_group(_ptr(x), m, k, _ptr(q), _ptr(sa), sa.shape[-1], _stream(x)))
+           lib().dg_quantize_per_token_group(_ptr(x), g, m, k, _ptr(q), _ptr(sa), sa.shape[-1], _stream(x)))
     return q, sa
 
 

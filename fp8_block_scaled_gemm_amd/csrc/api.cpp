@@ -14,7 +14,7 @@
 
 namespace dg {
 
-int launch_quant_token_group(const float* x, int64_t m, int64_t k, uint8_t* q, float* sa,
+int launch_quant_token_group(const float* x, int64_t groups, int64_t m, int64_t k, uint8_t* q, float* sa,
                              int64_t ld_sa, hipStream_t stream, int num_cus);
 int launch_quant_block(const float* w, int64_t groups, int64_t n, int64_t k, uint8_t* q, float* sb,
                        hipStream_t stream);
@@ -23,6 +23,8 @@ int launch_gemm(int layout, const uint8_t* a, const float* sa, int64_t ld_sa, co
                 int64_t groups, int64_t m, int64_t n, int64_t k, void* ws, size_t ws_bytes,
                 hipStream_t stream, int num_cus);
 size_t gemm_workspace_size(int64_t m, int64_t n, int64_t k, int64_t groups, int num_cus);
+void gemm_config_name(int layout, int64_t m, int64_t n, int64_t k, int64_t groups, int num_cus, char* buf,
+                      size_t len);
 
 static thread_local char g_msg[512] = "";
 
@@ -107,18 +109,19 @@ size_t dg_gemm_workspace_size(int64_t m, int64_t n, int64_t k, int64_t num_group
   return gemm_workspace_size(m, n, k, num_groups, cus);
 }
 
-int dg_quantize_per_token_group(const float* x, int64_t m, int64_t k, uint8_t* q, float* sa,
-                                int64_t ld_sa, dg_stream_t stream) {
-  DG_REQUIRE(m >= 0 && k > 0 && k % kGroup == 0, "quantize_per_token_group: need m >= 0, k > 0, k %% 128 == 0 (m=%lld k=%lld)",
+int dg_quantize_per_token_group(const float* x, int64_t num_groups, int64_t m, int64_t k, uint8_t* q,
+                                float* sa, int64_t ld_sa, dg_stream_t stream) {
+  DG_REQUIRE(num_groups >= 0 && m >= 0 && k > 0 && k % kGroup == 0,
+             "quantize_per_token_group: need groups >= 0, m >= 0, k > 0, k %% 128 == 0 (m=%lld k=%lld)",
              (long long)m, (long long)k);
   DG_REQUIRE(ld_sa >= m && ld_sa % 4 == 0, "quantize_per_token_group: need ld_sa >= m and ld_sa %% 4 == 0 (ld_sa=%lld)",
              (long long)ld_sa);
-  if (m == 0) return DG_OK;
+  if (m == 0 || num_groups == 0) return DG_OK;
   DG_REQUIRE(x && q && sa, "quantize_per_token_group: null pointer");
   DG_REQUIRE(aligned16(x) && aligned16(q) && aligned16(sa), "quantize_per_token_group: pointers must be 16-byte aligned");
   const int cus = effective_cus();
   if (cus < 0) return cus;
-  return launch_quant_token_group(x, m, k, q, sa, ld_sa, static_cast<hipStream_t>(stream), cus);
+  return launch_quant_token_group(x, num_groups, m, k, q, sa, ld_sa, static_cast<hipStream_t>(stream), cus);
 }
 
 int dg_quantize_per_block(const float* w, int64_t num_groups, int64_t n, int64_t k, uint8_t* q,
@@ -189,6 +192,16 @@ int dg_gemm_fp8_grouped_masked(const uint8_t* a, const float* sa, int64_t ld_sa,
   if (cus < 0) return cus;
   return launch_gemm(2, a, sa, ld_sa, b, sb, d, nullptr, masked_m, num_groups, m_max, n, k,
                      workspace, workspace ? workspace_bytes : 0, static_cast<hipStream_t>(stream), cus);
+}
+
+const char* dg_gemm_config_name(int layout, int64_t m, int64_t n, int64_t k, int64_t num_groups) {
+  static thread_local char buf[96];
+  buf[0] = 0;
+  if (layout < 0 || layout > 2 || m <= 0 || n <= 0 || k <= 0 || k % kGroup || num_groups <= 0) return buf;
+  const int cus = effective_cus();
+  if (cus < 0) return buf;
+  gemm_config_name(layout, m, n, k, num_groups, cus, buf, sizeof(buf));
+  return buf;
 }
 
 }  // extern "C"

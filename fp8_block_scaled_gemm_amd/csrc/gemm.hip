@@ -30,6 +30,8 @@
 //  * Small-m shapes split K over workgroups; the last-arriving workgroup of a
 //    tile sums the fp32 partials in fixed split order (deterministic) and stores
 //    bf16.
+#include <cstdio>
+
 #include "common.hpp"
 
 namespace dg {
@@ -123,7 +125,8 @@ __global__ __launch_bounds__(64 * (BN / WN) * (BM / WM)) void gemm_fp8_kernel(Ge
     __syncthreads();
     total_items = s_prefix[p.num_groups] * p.splits;
   } else {
-    total_items = p.tiles_m * p.tiles_n * p.num_groups * p.splits;
+    // contiguous: the expert comes from m_indices, not from the item index
+    total_items = p.tiles_m * p.tiles_n * (LAYOUT == kDense ? p.num_groups : 1) * p.splits;
   }
 
   // XCD-aware order: workgroup b runs on XCD b % 8; give each XCD a contiguous
@@ -288,6 +291,11 @@ __global__ __launch_bounds__(64 * (BN / WN) * (BM / WM)) void gemm_fp8_kernel(Ge
 #undef DG_STORE_STAGE
 
     // ---- split-K: last arriving workgroup sums partials in split order ---------
+    // The hand-off avoids device-scope fences (on a multi-XCD part they write back and
+    // invalidate whole L2 caches): partials are written with agent-scope stores, which
+    // write through the XCD's L2, completion is awaited with s_waitcnt before the
+    // arrival counter is bumped, and the last workgroup reads them back with
+    // agent-scope loads, which miss in its own (non-coherent) L2.
     if (p.splits > 1) {
       constexpr int kVals = C::kFragN * C::kFragM * 4;
       float* mine = p.ws + ((int64_t)t.tile_id * p.splits + t.split) * (int64_t)(kVals * NT);
@@ -296,33 +304,50 @@ __global__ __launch_bounds__(64 * (BN / WN) * (BM / WM)) void gemm_fp8_kernel(Ge
 #pragma unroll
         for (int j = 0; j < C::kFragM; ++j)
 #pragma unroll
-          for (int r = 0; r < 4; ++r) mine[((i * C::kFragM + j) * 4 + r) * NT + tid] = acc[i][j][r];
-      __threadfence();
+          for (int r = 0; r < 4; ++r)
+            __hip_atomic_store(mine + ((i * C::kFragM + j) * 4 + r) * NT + tid, acc[i][j][r], __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_AGENT);
+      __builtin_amdgcn_s_waitcnt(0);   // every partial store of this thread has completed
       __syncthreads();
       if (tid == 0) {
-        const unsigned prev = atomicAdd(p.counters + t.tile_id, 1u);
+        const unsigned prev =
+            __hip_atomic_fetch_add(p.counters + t.tile_id, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         s_flag = (prev == (unsigned)(p.splits - 1)) ? 1 : 0;
       }
       __syncthreads();
       if (!s_flag) continue;
-      __threadfence();
       const float* base = p.ws + (int64_t)t.tile_id * p.splits * (int64_t)(kVals * NT);
+      // fixed order: sum = p_0 + p_1 + ... + p_{S-1}; this workgroup's own partial comes from registers
+      v4f red[C::kFragN][C::kFragM];
+      for (int s = 0; s < p.splits; ++s) {
+        v4f v[C::kFragN][C::kFragM];
+        if (s == t.split) {
+#pragma unroll
+          for (int i = 0; i < C::kFragN; ++i)
+#pragma unroll
+            for (int j = 0; j < C::kFragM; ++j) v[i][j] = acc[i][j];
+        } else {
+          const float* src = base + (int64_t)s * (kVals * NT) + tid;
+#pragma unroll
+          for (int i = 0; i < C::kFragN; ++i)
+#pragma unroll
+            for (int j = 0; j < C::kFragM; ++j)
+#pragma unroll
+              for (int r = 0; r < 4; ++r)
+                v[i][j][r] = __hip_atomic_load(src + ((i * C::kFragM + j) * 4 + r) * NT, __ATOMIC_RELAXED,
+                                               __HIP_MEMORY_SCOPE_AGENT);
+        }
+#pragma unroll
+        for (int i = 0; i < C::kFragN; ++i)
+#pragma unroll
+          for (int j = 0; j < C::kFragM; ++j) red[i][j] = (s == 0) ? v[i][j] : red[i][j] + v[i][j];
+      }
 #pragma unroll
       for (int i = 0; i < C::kFragN; ++i)
 #pragma unroll
-        for (int j = 0; j < C::kFragM; ++j)
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const int e = ((i * C::kFragM + j) * 4 + r) * NT + tid;
-            float sum = 0.f;
-            for (int s = 0; s < p.splits; ++s) {
-              const float v = (s == t.split) ? acc[i][j][r]
-                                              : __builtin_nontemporal_load(base + (int64_t)s * (kVals * NT) + e);
-              sum = (s == 0) ? v : sum + v;
-            }
-            acc[i][j][r] = sum;
-          }
-      if (tid == 0) p.counters[t.tile_id] = 0u;   // leave the counter zeroed for the next call
+        for (int j = 0; j < C::kFragM; ++j) acc[i][j] = red[i][j];
+      if (tid == 0)   // leave the counter zeroed for the next call
+        __hip_atomic_store(p.counters + t.tile_id, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
 
     // ---- epilogue: fp32 -> bf16 (RNE), row-major store, edge masking ------------
@@ -422,6 +447,14 @@ static Plan make_plan(int64_t m, int64_t n, int64_t k, int64_t groups, int num_c
   return pl;
 }
 
+void gemm_config_name(int layout, int64_t m, int64_t n, int64_t k, int64_t groups, int num_cus, char* buf,
+                      size_t len) {
+  const Plan pl = make_plan(m, n, k, layout == kMasked ? groups : 1, num_cus, layout != kContiguous);
+  const LaunchInfo li = cfg_info<kDense>(pl.cfg);
+  const int waves = li.threads / 64;
+  snprintf(buf, len, "%dx%d/%dwaves/split%d", li.bn, li.bm, waves, pl.splits);
+}
+
 size_t gemm_workspace_size(int64_t m, int64_t n, int64_t k, int64_t groups, int num_cus) {
   return make_plan(m, n, k, groups, num_cus, true).ws_bytes;
 }
@@ -430,7 +463,7 @@ template <int LAYOUT>
 static int launch_layout(GemmParams p, const Plan& pl, hipStream_t stream, int num_cus) {
   const LaunchInfo li = cfg_info<LAYOUT>(pl.cfg);
   const int occ = occupancy(li);
-  int64_t items = (int64_t)pl.tiles_m * pl.tiles_n * p.num_groups * pl.splits;
+  int64_t items = (int64_t)pl.tiles_m * pl.tiles_n * (LAYOUT == kContiguous ? 1 : p.num_groups) * pl.splits;
   if (items > 0x7fffffffLL) return set_error(kUnsupported, "gemm: too many work items");
   int64_t grid = (int64_t)num_cus * occ;
   if (grid > items) grid = items;
@@ -448,8 +481,8 @@ int launch_gemm(int layout, const uint8_t* a, const float* sa, int64_t ld_sa, co
     return set_error(kUnsupported, "gemm: one group's operand must be < 2^31 bytes (m=%lld n=%lld k=%lld)",
                      (long long)m, (long long)n, (long long)k);
   const bool can_split = (layout != kContiguous) && ws != nullptr;
-  Plan pl = make_plan(m, n, k, layout == kDense ? 1 : groups, num_cus, can_split);
-  if (pl.splits > 1 && ws_bytes < pl.ws_bytes) pl = make_plan(m, n, k, layout == kDense ? 1 : groups, num_cus, false);
+  Plan pl = make_plan(m, n, k, layout == kMasked ? groups : 1, num_cus, can_split);
+  if (pl.splits > 1 && ws_bytes < pl.ws_bytes) pl = make_plan(m, n, k, layout == kMasked ? groups : 1, num_cus, false);
 
   GemmParams p{};
   p.a = a; p.sa = sa; p.b = b; p.sb = sb; p.d = d;

@@ -14,18 +14,18 @@
 namespace dg {
 
 // ---------------------------------------------------------------------------
-// 1 x 128 groups along K (activations).  A half-wave (32 lanes x 4 floats) owns
-// one group; consecutive half-waves take consecutive rows of the same K group so
-// that the MN-major scale stores are contiguous.
+// 1 x 128 groups along K (activations), for `groups` stacked (m, k) matrices.
+// A half-wave (32 lanes x 4 floats) owns one 128-wide group; consecutive
+// half-waves take consecutive rows of the same K group so that the MN-major
+// scale stores are contiguous.  Group index gi = (g * KB + kb) * m + row.
 // ---------------------------------------------------------------------------
 constexpr int kTokThreads = 256;
 constexpr int kTokUnroll = 4;   // groups per lane per iteration (loads in flight)
 
 __global__ __launch_bounds__(kTokThreads) void quant_token_group_kernel(
     const float* __restrict__ x, int64_t m, int64_t k, uint8_t* __restrict__ q,
-    float* __restrict__ sa, int64_t ld_sa) {
+    float* __restrict__ sa, int64_t ld_sa, int64_t groups) {
   const int lane = threadIdx.x & 31;
-  const int64_t groups = m * (k / kGroup);
   const int64_t half_waves = ((int64_t)gridDim.x * kTokThreads) >> 5;
   const int64_t first = ((int64_t)blockIdx.x * kTokThreads + threadIdx.x) >> 5;
 
@@ -35,24 +35,26 @@ __global__ __launch_bounds__(kTokThreads) void quant_token_group_kernel(
     for (int u = 0; u < kTokUnroll; ++u) {
       const int64_t gi = base + u * half_waves;
       if (gi < groups) {
-        const int64_t kb = gi / m, row = gi - kb * m;
+        const int64_t gkb = gi / m, row = gi - gkb * m;      // gkb = g * KB + kb
+        const int64_t kbc = k / kGroup, g = gkb / kbc, kb = gkb - g * kbc;
         v[u] = __builtin_nontemporal_load(
-            reinterpret_cast<const v4f*>(x + row * k + kb * kGroup) + lane);
+            reinterpret_cast<const v4f*>(x + (g * m + row) * k + kb * kGroup) + lane);
       }
     }
 #pragma unroll
     for (int u = 0; u < kTokUnroll; ++u) {
       const int64_t gi = base + u * half_waves;
       if (gi >= groups) break;   // uniform across the half-wave
-      const int64_t kb = gi / m, row = gi - kb * m;
+      const int64_t gkb = gi / m, row = gi - gkb * m;
+      const int64_t kbc = k / kGroup, g = gkb / kbc, kb = gkb - g * kbc;
       float amax = fmaxf(fmaxf(fabsf(v[u].x), fabsf(v[u].y)), fmaxf(fabsf(v[u].z), fabsf(v[u].w)));
 #pragma unroll
       for (int off = 16; off > 0; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off, 32));
       const float s = amax == 0.0f ? 1.0f : amax / kE4M3Max;
       const uint32_t packed = pack4_e4m3(clamp448(v[u].x / s), clamp448(v[u].y / s),
                                          clamp448(v[u].z / s), clamp448(v[u].w / s));
-      reinterpret_cast<uint32_t*>(q + row * k + kb * kGroup)[lane] = packed;
-      if (lane == 0) sa[kb * ld_sa + row] = s;
+      reinterpret_cast<uint32_t*>(q + (g * m + row) * k + kb * kGroup)[lane] = packed;
+      if (lane == 0) sa[gkb * ld_sa + row] = s;
     }
   }
 }
@@ -115,16 +117,16 @@ __global__ __launch_bounds__(kBlkThreads) void quant_block_kernel(
 // ---------------------------------------------------------------------------
 // Launchers (arguments already validated by the C ABI layer).
 // ---------------------------------------------------------------------------
-int launch_quant_token_group(const float* x, int64_t m, int64_t k, uint8_t* q, float* sa,
+int launch_quant_token_group(const float* x, int64_t mats, int64_t m, int64_t k, uint8_t* q, float* sa,
                              int64_t ld_sa, hipStream_t stream, int num_cus) {
-  const int64_t groups = m * (k / kGroup);
+  const int64_t groups = mats * m * (k / kGroup);
   const int64_t groups_per_block = kTokThreads / 32;
   int64_t blocks = (groups + groups_per_block * kTokUnroll - 1) / (groups_per_block * kTokUnroll);
   const int64_t cap = (int64_t)num_cus * 16;   // enough resident waves to cover HBM latency
   if (blocks > cap) blocks = cap;
   if (blocks < 1) blocks = 1;
   hipLaunchKernelGGL(quant_token_group_kernel, dim3((unsigned)blocks), dim3(kTokThreads), 0,
-                     stream, x, m, k, q, sa, ld_sa);
+                     stream, x, m, k, q, sa, ld_sa, groups);
   const hipError_t e = hipGetLastError();
   return e == hipSuccess ? kOk : set_error(kHip, "quantize_per_token_group launch: %s", hipGetErrorString(e));
 }

@@ -69,20 +69,23 @@ const char* dg_status_string(int status);
 const char* dg_last_error_message(void);
 
 /*
- * Per-token-group activation quantizer (1 x 128).
+ * Per-token-group activation quantizer (1 x 128), for num_groups stacked (m, k)
+ * matrices (num_groups = 1 for a plain activation matrix; the masked MoE layout
+ * uses one group per expert).
  * Fine-grained scaling as in DeepSeek-V3 (机器之心 report, opening section),
  * E4M3 data (ai.abqq.net summary, section 3).  For each row r and K group kb:
  *   amax = max |x[r, 128kb .. 128kb+127]|
  *   s    = amax / 448 (IEEE fp32 division; s = 1 when amax == 0)
  *   q    = E4M3 round-to-nearest-even, saturating, of fl32(x / s) (IEEE division)
- * x  : fp32 (m, k) row-major, read only.
- * q  : E4M3 bytes (m, k) row-major, written.
- * sa : fp32 scales, written at sa[kb * ld_sa + r] for r < m; entries r >= m untouched.
- * Errors: DG_ERR_INVALID_ARG for null/misaligned pointers, m < 0, k % 128 != 0,
- * ld_sa < m or ld_sa % 4 != 0.  Output is bit-exact (the result is unique).
+ * x  : fp32 (num_groups, m, k) row-major, read only.
+ * q  : E4M3 bytes (num_groups, m, k) row-major, written.
+ * sa : fp32 scales, MN-major per group: written at sa[(g * (k/128) + kb) * ld_sa + r]
+ *      for r < m; entries r >= m are untouched.
+ * Errors: DG_ERR_INVALID_ARG for null/misaligned pointers, m < 0, num_groups < 0,
+ * k % 128 != 0, ld_sa < m or ld_sa % 4 != 0.  Output is bit-exact (the result is unique).
  */
-int dg_quantize_per_token_group(const float* x, int64_t m, int64_t k, uint8_t* q, float* sa,
-                                int64_t ld_sa, dg_stream_t stream);
+int dg_quantize_per_token_group(const float* x, int64_t num_groups, int64_t m, int64_t k, uint8_t* q,
+                                float* sa, int64_t ld_sa, dg_stream_t stream);
 
 /*
  * Per-block weight quantizer (128 x 128), for num_groups stacked (n, k) matrices.
@@ -179,6 +182,12 @@ int64_t dg_get_scale_ld(int64_t rows);
  * split-K for the given shape (m = rows per group; num_groups = 1 for the
  * normal GEMM).  0 means split-K is never used for that shape. */
 size_t dg_gemm_workspace_size(int64_t m, int64_t n, int64_t k, int64_t num_groups);
+
+/* Name of the tile configuration and K split the GEMM picks for a shape, as
+ * "BNxBM/WNxWM/splitS" (static thread-local string), assuming a large enough
+ * workspace.  layout: 0 normal, 1 contiguous-grouped, 2 masked-grouped (m = rows
+ * per group).  For profiling and reports; returns "" for invalid arguments. */
+const char* dg_gemm_config_name(int layout, int64_t m, int64_t n, int64_t k, int64_t num_groups);
 
 #ifdef __cplusplus
 }

@@ -178,3 +178,21 @@ def test_quant_errors():
         dg.dg_quantize_per_token_group(x)
     q, sa = dg.dg_quantize_per_token_group(torch.zeros((0, 128), dtype=torch.float32, device=device()))
     assert q.shape == (0, 128)
+
+
+def test_token_group_batched():
+    """(G, M, K) input: per-group MN-major scales (G, K/128, ld_sa), bytes per group."""
+    say("quant token group batched")
+    rng = inputs.rng_for("quant_batched")
+    x = inputs.normal(rng, (3, 77, 256))
+    x[1] *= np.float32(30.0)
+    ld = dg.dg_get_scale_ld(77) + 4
+    sa = torch.full((3, 2, ld), float("nan"), dtype=torch.float32, device=device())
+    q, sa = dg.dg_quantize_per_token_group(to_dev(x), sa=sa)
+    torch.cuda.synchronize()
+    q, sa = q.cpu().numpy(), sa.cpu().numpy()
+    assert np.all(np.isnan(sa[:, :, 77:]))
+    for g in range(3):
+        qo, so = oracle.quant.quantize_per_token_group(x[g])
+        assert np.array_equal(q[g], qo)
+        assert np.array_equal(bits32(sa[g, :, :77].T), bits32(so))
