@@ -25,6 +25,8 @@ COMMON_FLAGS = [
     "-fno-fast-math",
     # keep the compiler from forming packed fp32 ops (v_pk_*_f32)
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # keep MFMA results in VGPRs: the promotion FMAs read them directly (no AGPR copy)
+    "-mllvm", "-amdgpu-mfma-vgpr-form",
     "-Wno-unused-command-line-argument",
     f"-I{os.path.join(ROOT, 'include')}",
 ]

@@ -9,28 +9,35 @@
 //
 // Design for gfx950 (none of the Hopper-specific structure of the pages):
 //  * One v_mfma_scale_f32_16x16x128_f8f6f4 covers a whole 128-deep K block of a
-//    16x16 output fragment, so the level-1 partial of a K block is exactly one
-//    MFMA into a zero accumulator, and the level-2 promotion is one VALU FMA per
-//    output element:  acc += P * fl32(sa * sb).  The promotion of one fragment
-//    overlaps the next fragments' MFMAs.  The MFMA's own E8M0 block scales are
-//    left neutral (2^0): the fine-grained scales are arbitrary fp32 values.
+//    16x16 output fragment, so the level-1 partial of a K block is one MFMA into a
+//    zero accumulator and the level-2 promotion is one VALU FMA per output:
+//    acc += P * fl32(sa * sb).  The MFMA's own E8M0 block scales stay neutral
+//    (2^0): the fine-grained scales are arbitrary fp32 values.  The library is
+//    built with MFMA results in VGPRs (no AGPR round trip before the FMA), and the
+//    large tiles run two waves per SIMD so that one wave's promotion FMAs overlap
+//    the other's MFMAs.
 //  * MFMA operand A is the weight tile (rows n), operand B the activation tile
-//    (rows m): each lane then holds 4 consecutive n of one row m, so the bf16
-//    epilogue stores 8 contiguous bytes per lane and the promotion scale is one
-//    value per lane and fragment.
-//  * Operand tiles (BN x 128 and BM x 128 bytes per K block) are staged in LDS
-//    with 16-byte coalesced global loads, double-buffered, with an XOR swizzle of
-//    the 16-byte chunks (chunk c of row r lives at slot c ^ (r & 7)) so the
-//    fragment reads are free of bank conflicts.
-//  * A persistent grid (at most the CU cap x occupancy) walks work items
-//    (group, m-block, n-block, k-split) - the contiguous layout reads each
-//    m-block's expert from m_indices, the masked layout reads masked_m on the
-//    device and skips empty m-blocks - with an XCD-aware item order so that
-//    workgroups sharing a weight panel run on the same XCD (same L2).
+//    (rows m): each lane holds 4 consecutive n of one row m, so the promotion
+//    scale is one value per lane and fragment and the bf16 epilogue stores 8
+//    contiguous bytes per lane.
+//  * Operand tiles (BN x 128 and BM x 128 bytes per K block) go straight from
+//    global memory into LDS (buffer_load_dwordx4 ... lds: a 32-bit per-lane offset,
+//    the K-block offset in an SGPR, no staging registers) in a
+//    ring of STAGES buffers, each its own __shared__ object so that the compiler's
+//    wait insertion can tell them apart.  Row r's 16-byte chunk c lives at slot
+//    c ^ f(r), f(r) = (r & 7) ^ ((r >> 3) & 1): the 8 lanes of a DMA that fill one
+//    row write one contiguous 128-byte line, and a fragment read (16 consecutive
+//    rows, one logical chunk) touches 16 distinct 16-byte bank groups.
+//  * A persistent grid (at most CU cap x occupancy) walks work items (group,
+//    m-block, n-block, k-split) - the contiguous layout reads each m-block's
+//    expert from m_indices, the masked layout reads masked_m on the device and
+//    skips empty m-blocks - in an XCD-aware order (workgroups of one XCD take
+//    neighbouring items, so they share weight panels in their L2).
 //  * Small-m shapes split K over workgroups; the last-arriving workgroup of a
 //    tile sums the fp32 partials in fixed split order (deterministic) and stores
 //    bf16.
 #include <cstdio>
+#include <type_traits>
 
 #include "common.hpp"
 
@@ -61,52 +68,110 @@ struct GemmParams {
   int nb128;        // ceil(n / 128): weight-scale rows per group
 };
 
-template <int BN, int BM, int WN, int WM>
-struct TileCfg {
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) void lds_void;
+// Buffer resource word 3 for raw (untyped, stride 0) buffer accesses on gfx9-family parts.
+constexpr int kBufferWord3 = 0x00020000;
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int64_t bytes) {
+  const int n = bytes > 0x7fffffffLL ? 0x7fffffff : (int)bytes;
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, n, kBufferWord3);
+}
+
+// LDS DMA: every active lane copies 16 (4) bytes from rsrc + voff + soff into lds + lane * 16 (4)
+// (buffer_load_dword{,x4} ... lds; out-of-range offsets read zeros).
+__device__ __forceinline__ void lds_dma16(__amdgpu_buffer_rsrc_t rsrc, void* lds, uint32_t voff, int soff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void*)lds, 16, voff, soff, 0, 0);
+}
+__device__ __forceinline__ void lds_dma4(__amdgpu_buffer_rsrc_t rsrc, void* lds, uint32_t voff, int soff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void*)lds, 4, voff, soff, 0, 0);
+}
+template <int V>
+using IC = std::integral_constant<int, V>;
+
+template <int BN_, int BM_, int WN_, int WM_, int STAGES_>
+struct Cfg {
+  static constexpr int BN = BN_, BM = BM_, WN = WN_, WM = WM_, STAGES = STAGES_;
   static constexpr int kWavesN = BN / WN;
   static constexpr int kWavesM = BM / WM;
-  static constexpr int kThreads = 64 * kWavesN * kWavesM;
+  static constexpr int kWaves = kWavesN * kWavesM;
+  static constexpr int kThreads = 64 * kWaves;
   static constexpr int kFragN = WN / 16;
   static constexpr int kFragM = WM / 16;
-  static constexpr int kStageBytes = (BN + BM) * kGroup;
-  static constexpr int kChunksB = BN * 8;          // 16-byte chunks per K block
-  static constexpr int kChunksA = BM * 8;
-  static constexpr int kLoadsB = kChunksB / kThreads;
-  static constexpr int kLoadsA = kChunksA / kThreads;
-  static_assert(kChunksB % kThreads == 0 && kChunksA % kThreads == 0, "tile/threads mismatch");
+  static constexpr int kSaOffset = (BN + BM) * kGroup;         // BM activation scales follow the tiles
+  static constexpr int kSbOffset = kSaOffset + BM * 4;          // then the weight scales (adjacent)
+  static constexpr int kSbCount = (BN + 127) / 128;             // 128-row weight blocks of a tile
+  static constexpr int kSbWaveBytes = 16 * ((kSbCount * 4 + 15) / 16);   // one copy per wave
+  static constexpr int kStageBytes = kSbOffset + kWaves * kSbWaveBytes;
+  static constexpr int kDmaRows = 8;                          // one DMA instruction = 8 rows x 128 B
+  static constexpr int kDmaB = BN / kDmaRows;                 // DMA instructions per stage, weights
+  static constexpr int kDma = (BN + BM) / kDmaRows;           // ... weights + activations
+  static constexpr int kDmaPerWave = kDma / kWaves;
+  // activation scales: BM floats = BM/4 16-byte chunks, spread over the waves' lanes
+  static constexpr int kSaLanesPerWave = (BM / 4 + kWaves - 1) / kWaves;
+  // vector-memory instructions one thread issues per stage: operand DMAs + the two scale DMAs
+  static constexpr int kVmPerStage = kDmaPerWave + 2;
+  static_assert(kDma % kWaves == 0 && kDmaB % kWaves == 0, "DMA instructions must split evenly over waves");
   static_assert(WN % 16 == 0 && WM % 16 == 0 && 128 % WN == 0, "wave tile must be 16-aligned, WN | 128");
+  static_assert(STAGES >= 2 && STAGES <= 4, "2..4 stages");
+  static_assert(kVmPerStage * (STAGES - 1) < 64, "vmcnt range");
+  static_assert(kSaLanesPerWave <= 64 && BM % 4 == 0, "scale DMA shape");
 };
 
-typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+// LDS slot of 16-byte chunk c of tile row r.  f depends on r mod 16 only, so every fragment
+// of a lane shares one pattern and fragment addresses differ by immediates.
+__device__ __forceinline__ int swz_row(int r) { return (r & 7) ^ ((r >> 3) & 1); }
+__device__ __forceinline__ int lds_off(int r, int c) { return r * kGroup + ((c ^ swz_row(r)) << 4); }
 
 __device__ __forceinline__ v8i make_v8i(u32x4 lo, u32x4 hi) {
   return v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
 }
 
-__device__ __forceinline__ int swz(int row, int chunk) { return row * kGroup + ((chunk ^ (row & 7)) << 4); }
+// s_waitcnt vmcnt(N) (gfx9 encoding; expcnt and lgkmcnt left at their maxima).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+// Wait until at most `younger` stage groups of PER vector-memory instructions remain outstanding.
+template <int PER, int MAXG>
+__device__ __forceinline__ void wait_groups(int younger) {
+  if constexpr (MAXG >= 3) {
+    if (younger >= 3) { wait_vmcnt<3 * PER>(); return; }
+  }
+  if constexpr (MAXG >= 2) {
+    if (younger >= 2) { wait_vmcnt<2 * PER>(); return; }
+  }
+  if constexpr (MAXG >= 1) {
+    if (younger >= 1) { wait_vmcnt<PER>(); return; }
+  }
+  wait_vmcnt<0>();
+}
 
-// Work item -> tile coordinates.  Returns false when the item maps to nothing.
-struct Tile {
-  int g, mb, nbt, split;
-  int m_valid;      // rows of this group that may be stored (dense: m; masked: masked count)
-  int tile_id;      // index of the (g, mb, nbt) tile for split-K bookkeeping
+struct TileCoord {
+  int g, mb, nbt, split, m_valid, tile_id;
 };
 
-template <int BN, int BM, int WN, int WM, int LAYOUT>
-__global__ __launch_bounds__(64 * (BN / WN) * (BM / WM)) void gemm_fp8_kernel(GemmParams p) {
-  using C = TileCfg<BN, BM, WN, WM>;
+template <class C, int LAYOUT>
+__global__ __launch_bounds__(C::kThreads) void gemm_fp8_kernel(GemmParams p) {
   constexpr int NT = C::kThreads;
-  __shared__ __attribute__((aligned(16))) uint8_t smem[2][C::kStageBytes];
+  constexpr int S = C::STAGES;
+  __shared__ __attribute__((aligned(1024))) uint8_t st0[C::kStageBytes];
+  __shared__ __attribute__((aligned(1024))) uint8_t st1[C::kStageBytes];
+  __shared__ __attribute__((aligned(1024))) uint8_t st2[S > 2 ? C::kStageBytes : 16];
+  __shared__ __attribute__((aligned(1024))) uint8_t st3[S > 3 ? C::kStageBytes : 16];
   __shared__ int s_prefix[LAYOUT == kMasked ? 1025 : 1];
   __shared__ int s_flag;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform (scalar) from here on
   const int wave_n = wave % C::kWavesN;
   const int wave_m = wave / C::kWavesN;
   const int l16 = lane & 15;
   const int g4 = lane >> 4;
+  const int wn0 = wave_n * C::WN;
+  const int wm0 = wave_m * C::WM;
 
   // ---- total work items -------------------------------------------------------
   int total_items;
@@ -118,7 +183,7 @@ __global__ __launch_bounds__(64 * (BN / WN) * (BM / WM)) void gemm_fp8_kernel(Ge
       for (int g = 0; g < p.num_groups; ++g) {
         int mv = p.masked_m[g];
         mv = mv < 0 ? 0 : (mv > p.m ? p.m : mv);
-        acc += ((mv + BM - 1) / BM) * p.tiles_n;
+        acc += ((mv + C::BM - 1) / C::BM) * p.tiles_n;
         s_prefix[g + 1] = acc;
       }
     }
@@ -137,29 +202,39 @@ __global__ __launch_bounds__(64 * (BN / WN) * (BM / WM)) void gemm_fp8_kernel(Ge
 
   for (int item = wg; item < total_items; item += grid) {
     // ---- decode the item ------------------------------------------------------
-    Tile t;
+    TileCoord t;
     t.split = item % p.splits;
     int rest = item / p.splits;
     if constexpr (LAYOUT == kMasked) {
       int g = 0;
       while (s_prefix[g + 1] <= rest) ++g;
       rest -= s_prefix[g];
+      const int mblocks = (s_prefix[g + 1] - s_prefix[g]) / p.tiles_n;
       t.g = g;
-      t.mb = rest % ((s_prefix[g + 1] - s_prefix[g]) / p.tiles_n);
-      t.nbt = rest / ((s_prefix[g + 1] - s_prefix[g]) / p.tiles_n);
+      t.mb = rest % mblocks;
+      t.nbt = rest / mblocks;
       int mv = p.masked_m[g];
       t.m_valid = mv < 0 ? 0 : (mv > p.m ? p.m : mv);
       t.tile_id = (g * p.tiles_m + t.mb) * p.tiles_n + t.nbt;
     } else {
-      t.mb = rest % p.tiles_m;
-      rest /= p.tiles_m;
-      t.nbt = rest % p.tiles_n;
-      t.g = rest / p.tiles_n;
+      // grouped order: runs of kGroupM m-tiles x all n-tiles, m fastest inside a run, so the
+      // grid/8 consecutive items one XCD takes per round cover ~8 activation panels and a few
+      // weight panels (both reused from that XCD's L2)
+      constexpr int kGroupM = 8;
+      const int per_group = p.tiles_m * p.tiles_n;
+      t.g = rest / per_group;
+      const int tl = rest - t.g * per_group;
+      const int run = tl / (kGroupM * p.tiles_n);
+      const int first_m = run * kGroupM;
+      const int run_m = (p.tiles_m - first_m) < kGroupM ? (p.tiles_m - first_m) : kGroupM;
+      const int in_run = tl - run * (kGroupM * p.tiles_n);
+      t.mb = first_m + in_run % run_m;
+      t.nbt = in_run / run_m;
       t.m_valid = p.m;
       t.tile_id = (t.g * p.tiles_m + t.mb) * p.tiles_n + t.nbt;
     }
-    const int m0 = t.mb * BM;
-    const int n0 = t.nbt * BN;
+    const int m0 = t.mb * C::BM;
+    const int n0 = t.nbt * C::BN;
     int expert = t.g;
     if constexpr (LAYOUT == kContiguous) {
       expert = p.m_indices[m0];
@@ -168,41 +243,43 @@ __global__ __launch_bounds__(64 * (BN / WN) * (BM / WM)) void gemm_fp8_kernel(Ge
     const int kb_begin = t.split * p.kb_per_split;
     int kb_end = kb_begin + p.kb_per_split;
     if (kb_end > p.kb_total) kb_end = p.kb_total;
+    const int nk = kb_end - kb_begin;
 
     const uint8_t* a_g = p.a + (LAYOUT == kMasked ? (int64_t)t.g * p.a_gstride : 0);
     const float* sa_g = p.sa + (LAYOUT == kMasked ? (int64_t)t.g * p.sa_gstride : 0);
     const uint8_t* b_g = p.b + (int64_t)expert * p.b_gstride;
     const float* sb_g = p.sb + (int64_t)expert * p.sb_gstride;
-    const int m_last = p.m - 1;   // clamp target for edge rows (rows per group)
 
-    // ---- global -> register staging (thread t: chunk t % 8 of rows t / 8 + u * NT / 8) ----
-    // 32-bit offsets: every operand matrix of one group is < 2^31 bytes (checked on the host).
-    constexpr int kRowStep = NT / 8;
-    const int ch = tid & 7;
-    const int rbase = tid >> 3;
-    int offB[C::kLoadsB], offA[C::kLoadsA];
-#pragma unroll
-    for (int u = 0; u < C::kLoadsB; ++u) {
-      int grow = n0 + rbase + u * kRowStep;
-      grow = grow < p.n ? grow : p.n - 1;
-      offB[u] = grow * p.k + ch * 16;
-    }
-#pragma unroll
-    for (int u = 0; u < C::kLoadsA; ++u) {
-      int grow = m0 + rbase + u * kRowStep;
-      grow = grow <= m_last ? grow : m_last;
-      offA[u] = grow * p.k + ch * 16;
-    }
-    const int lds_st = swz(rbase, ch);   // + u * kRowStep * 128 (kRowStep is a multiple of 8)
-    // per-lane activation-scale rows and the wave's weight-scale block
-    int sa_row[C::kFragM];
-#pragma unroll
-    for (int j = 0; j < C::kFragM; ++j) {
-      const int r = m0 + wave_m * WM + 16 * j + l16;
-      sa_row[j] = r <= m_last ? r : m_last;
-    }
-    const int nb_w = (n0 + wave_n * WN) >> 7;
-    const float* sb_row = sb_g + (int64_t)(nb_w < p.nb128 ? nb_w : p.nb128 - 1) * p.kb_total;
+    // DMA instruction u of this wave fills tile rows [8q, 8q+8) of a stage, q = wave + kWaves*u:
+    // weights for u < kDmaB / kWaves, activations after.  Lane i writes slot i of that 1 KB (tile
+    // row 8q + i/8, slot i%8), so it loads logical chunk (i%8) ^ f(row).  Each operand has one
+    // buffer resource based at the tile's first row and sized to the rows that exist: the hardware
+    // range check returns zeros for rows past the N or M edge (those outputs are never stored).
+    constexpr int kBandRows = 8 * C::kWaves;
+    constexpr int kBandsB = C::kDmaB / C::kWaves;
+    const int dma_row = 8 * wave + (lane >> 3);   // tile-local row within band 0 (f(row) is band-invariant)
+    const uint32_t dma_off = (uint32_t)dma_row * (uint32_t)p.k + (uint32_t)(((lane & 7) ^ swz_row(dma_row)) << 4);
+    const uint32_t band_step = (uint32_t)kBandRows * (uint32_t)p.k;
+    const __amdgpu_buffer_rsrc_t rs_b =
+        make_rsrc(b_g + (int64_t)n0 * p.k, p.n > n0 ? (int64_t)(p.n - n0) * p.k : 0);
+    const __amdgpu_buffer_rsrc_t rs_a =
+        make_rsrc(a_g + (int64_t)m0 * p.k, p.m > m0 ? (int64_t)(p.m - m0) * p.k : 0);
+    // activation scales: lanes [kSaLanesPerWave*wave, +kSaLanesPerWave) of the BM/4 16-byte chunks
+    // of sa[kb][m0 .. m0+BM); chunks are clamped to the caller's ld_sa row (rows >= m are never stored)
+    const int sa_lane = wave * C::kSaLanesPerWave + lane;
+    const bool sa_active = lane < C::kSaLanesPerWave && sa_lane < C::BM / 4;
+    int sa_src_row = m0 + 4 * sa_lane;
+    sa_src_row = sa_src_row + 4 <= p.ld_sa ? sa_src_row : (int)p.ld_sa - 4;
+    const uint32_t sa_src = (uint32_t)sa_src_row * 4u;   // byte offset within the kb row
+    // weight scales: lane i < kSbCount of every wave fetches the scale of weight block n0/128 + i
+    // into the wave's own copy (keeps the per-wave vmcnt accounting uniform)
+    const bool sb_active = lane < C::kSbCount;
+    int sb_blk = (n0 >> 7) + lane;
+    sb_blk = sb_blk < p.nb128 ? sb_blk : p.nb128 - 1;
+    const uint32_t sb_src = (uint32_t)sb_blk * (uint32_t)p.kb_total * 4u;
+    const int sb_idx = ((n0 + wn0) >> 7) - (n0 >> 7);   // this wave's block within the tile
+    const __amdgpu_buffer_rsrc_t rs_sa = make_rsrc(sa_g, (int64_t)p.kb_total * p.ld_sa * 4);
+    const __amdgpu_buffer_rsrc_t rs_sb = make_rsrc(sb_g, (int64_t)p.nb128 * p.kb_total * 4);
 
     v4f acc[C::kFragN][C::kFragM];
 #pragma unroll
@@ -210,85 +287,109 @@ __global__ __launch_bounds__(64 * (BN / WN) * (BM / WM)) void gemm_fp8_kernel(Ge
 #pragma unroll
       for (int j = 0; j < C::kFragM; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
 
-    u32x4 regB[C::kLoadsB], regA[C::kLoadsA];
-    float sa_cur[C::kFragM], sa_next[C::kFragM];
-    float sb_cur, sb_next;
-
-#define DG_LOAD_STAGE(KB)                                                                     \
-  do {                                                                                        \
-    const uint8_t* gb = b_g + (int64_t)(KB) * kGroup;                                         \
-    const uint8_t* ga = a_g + (int64_t)(KB) * kGroup;                                         \
-    _Pragma("unroll") for (int u = 0; u < C::kLoadsB; ++u) regB[u] =                         \
-        *reinterpret_cast<const u32x4*>(gb + offB[u]);                                        \
-    _Pragma("unroll") for (int u = 0; u < C::kLoadsA; ++u) regA[u] =                         \
-        *reinterpret_cast<const u32x4*>(ga + offA[u]);                                        \
-    _Pragma("unroll") for (int j = 0; j < C::kFragM; ++j) sa_next[j] =                       \
-        sa_g[(int64_t)(KB) * p.ld_sa + sa_row[j]];                                            \
-    sb_next = sb_row[(KB)];                                                                   \
-  } while (0)
-#define DG_STORE_STAGE(STG)                                                                   \
-  do {                                                                                        \
-    uint8_t* sdst = smem[(STG)] + lds_st;                                                     \
-    _Pragma("unroll") for (int u = 0; u < C::kLoadsB; ++u)                                    \
-        *reinterpret_cast<u32x4*>(sdst + u * kRowStep * kGroup) = regB[u];                    \
-    _Pragma("unroll") for (int u = 0; u < C::kLoadsA; ++u)                                    \
-        *reinterpret_cast<u32x4*>(sdst + BN * kGroup + u * kRowStep * kGroup) = regA[u];      \
-  } while (0)
-
-    __syncthreads();   // previous tile's readers are done with both stages
-    DG_LOAD_STAGE(kb_begin);
-    DG_STORE_STAGE(0);
+    // Issue the stage group of local K block tk (absolute kb_begin + tk) into ring slot SLOT:
+    // kDmaPerWave operand DMAs and one scale DMA per thread (the vmcnt accounting counts
+    // kVmPerStage per group); the weight scale is a scalar load.
+    auto issue = [&](int tk, auto slot_c) {
+      constexpr int slot = decltype(slot_c)::value;
+      const int kb = kb_begin + tk;
+      uint8_t* sbase = slot == 0 ? st0 : slot == 1 ? st1 : slot == 2 ? st2 : st3;
 #pragma unroll
-    for (int j = 0; j < C::kFragM; ++j) sa_cur[j] = sa_next[j];
-    sb_cur = sb_next;
-    __syncthreads();
+      for (int u = 0; u < C::kDmaPerWave; ++u) {
+        const int q = wave + C::kWaves * u;
+        const bool is_b = u < kBandsB;
+        lds_dma16(is_b ? rs_b : rs_a, sbase + q * (C::kDmaRows * kGroup),
+                  dma_off + (uint32_t)(is_b ? u : u - kBandsB) * band_step, kb * kGroup);
+      }
+      if (sa_active)
+        lds_dma16(rs_sa, sbase + C::kSaOffset + 16 * wave * C::kSaLanesPerWave, sa_src, kb * (int)p.ld_sa * 4);
+      if (sb_active)
+        lds_dma4(rs_sb, sbase + C::kSbOffset + wave * C::kSbWaveBytes, sb_src, kb * 4);
+    };
+    auto issue_rt = [&](int tk, int slot) {
+      if (slot == 0) issue(tk, IC<0>{});
+      else if (slot == 1) issue(tk, IC<1>{});
+      else if (slot == 2) issue(tk, IC<(S > 2 ? 2 : 0)>{});
+      else issue(tk, IC<(S > 3 ? 3 : 0)>{});
+    };
 
-    int stage = 0;
-    for (int kb = kb_begin; kb < kb_end; ++kb) {
-      const bool more = kb + 1 < kb_end;
-      if (more) DG_LOAD_STAGE(kb + 1);
-
-      const uint8_t* sB = smem[stage];
-      const uint8_t* sA = smem[stage] + BN * kGroup;
-      // activation fragments (MFMA operand B), all of the wave's m-fragments
+    // Level-1 MFMA partials of the K block in ring slot SLOT and their level-2 promotion.
+    // The B fragments (activations) and scales of the K block are read from LDS once; the A
+    // fragments (weights) are streamed, fragment i+1 being read while fragment i's MFMAs run.
+    // Over the flat sequence q = (i, j) the MFMA of q is issued before the promotion FMAs of
+    // q-1, so the matrix core does not wait for a partial the VALU is about to consume.
+    auto compute = [&](auto slot_c) {
+      constexpr int slot = decltype(slot_c)::value;
+      const uint8_t* sbase = slot == 0 ? st0 : slot == 1 ? st1 : slot == 2 ? st2 : st3;
+      // A operand (weights) rows wn0 + 16i + l16, B operand (activations) rows wm0 + 16j + l16; a lane
+      // reads logical chunks 2*g4 and 2*g4+1 (K bytes 32*g4 .. 32*g4+31) of its row.  The second
+      // chunk's slot differs from the first's in bit 0 only: address ^ 16.
+      const int lane_off = lds_off(l16, 2 * g4);   // == lds_off(16x + l16, 2*g4) - 16x*128
+      auto read_a = [&](int i) {
+        const int off = (wn0 + 16 * i) * kGroup + lane_off;
+        return make_v8i(*reinterpret_cast<const u32x4*>(sbase + off),
+                        *reinterpret_cast<const u32x4*>(sbase + (off ^ 16)));
+      };
       v8i bop[C::kFragM];
 #pragma unroll
       for (int j = 0; j < C::kFragM; ++j) {
-        const int row = wave_m * WM + 16 * j + l16;
-        const u32x4 lo = *reinterpret_cast<const u32x4*>(sA + swz(row, 2 * g4));
-        const u32x4 hi = *reinterpret_cast<const u32x4*>(sA + swz(row, 2 * g4 + 1));
-        bop[j] = make_v8i(lo, hi);
+        const int off = (C::BN + wm0 + 16 * j) * kGroup + lane_off;
+        bop[j] = make_v8i(*reinterpret_cast<const u32x4*>(sbase + off),
+                          *reinterpret_cast<const u32x4*>(sbase + (off ^ 16)));
       }
+      const float* sa_l = reinterpret_cast<const float*>(sbase + C::kSaOffset);
+      const float sbv = sa_l[C::BM + wave * (C::kSbWaveBytes / 4) + sb_idx];   // this wave's copy
       float scale[C::kFragM];
 #pragma unroll
-      for (int j = 0; j < C::kFragM; ++j) scale[j] = sa_cur[j] * sb_cur;   // fl32(sa * sb)
+      for (int j = 0; j < C::kFragM; ++j) scale[j] = sa_l[wm0 + 16 * j + l16] * sbv;   // fl32(sa * sb)
 
+      constexpr int Q = C::kFragN * C::kFragM;
+      v8i aop[2];
+      aop[0] = read_a(0);
+      v4f part[2];
 #pragma unroll
-      for (int i = 0; i < C::kFragN; ++i) {
-        const int row = wave_n * WN + 16 * i + l16;
-        const u32x4 lo = *reinterpret_cast<const u32x4*>(sB + swz(row, 2 * g4));
-        const u32x4 hi = *reinterpret_cast<const u32x4*>(sB + swz(row, 2 * g4 + 1));
-        const v8i aop = make_v8i(lo, hi);
+      for (int q = 0; q <= Q; ++q) {
+        if (q < Q) {
+          const int i = q / C::kFragM, j = q % C::kFragM;
+          if (j == 0 && i + 1 < C::kFragN) aop[(i + 1) & 1] = read_a(i + 1);
+          part[q & 1] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+              aop[i & 1], bop[j], v4f{0.f, 0.f, 0.f, 0.f}, 0, 0, 0, 127, 0, 127);
+        }
+        if (q > 0) {
+          const int i = (q - 1) / C::kFragM, j = (q - 1) % C::kFragM;
 #pragma unroll
-        for (int j = 0; j < C::kFragM; ++j) {
-          const v4f part = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-              aop, bop[j], v4f{0.f, 0.f, 0.f, 0.f}, 0, 0, 0, 127, 0, 127);
-#pragma unroll
-          for (int r = 0; r < 4; ++r) acc[i][j][r] = __builtin_fmaf(part[r], scale[j], acc[i][j][r]);
+          for (int r = 0; r < 4; ++r)
+            acc[i][j][r] = __builtin_fmaf(part[(q - 1) & 1][r], scale[j], acc[i][j][r]);
+        }
+        if (q > 0 && q < Q) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA of q
+          __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);   // FMAs of q-1
         }
       }
+    };
 
-      if (more) {
-        DG_STORE_STAGE(stage ^ 1);
+    // ---- main loop: ring of S stages, one barrier per K block -------------------
+    __syncthreads();   // the previous tile's readers are done with every stage
 #pragma unroll
-        for (int j = 0; j < C::kFragM; ++j) sa_cur[j] = sa_next[j];
-        sb_cur = sb_next;
+    for (int s = 0; s < S - 1; ++s)
+      if (s < nk) issue_rt(s, s);
+    for (int t0 = 0; t0 < nk; t0 += S) {
+#pragma unroll
+      for (int s = 0; s < S; ++s) {
+        const int tk = t0 + s;
+        if (tk >= nk) break;
+        // K block tk landed for this thread (groups tk+1 .. min(tk+S-2, nk-1) may still fly) ...
+        const int younger = (nk - 1 - tk) < (S - 2) ? (nk - 1 - tk) : (S - 2);
+        wait_groups<C::kVmPerStage, S - 2>(younger);
+        // ... and for every thread; also everyone finished computing tk-1, whose slot is refilled next
+        __syncthreads();
+        if (tk + S - 1 < nk) issue_rt(tk + S - 1, (s + S - 1) % S);
+        if (s == 0) compute(IC<0>{});
+        else if (s == 1) compute(IC<1>{});
+        else if (s == 2) compute(IC<(S > 2 ? 2 : 0)>{});
+        else compute(IC<(S > 3 ? 3 : 0)>{});
       }
-      __syncthreads();
-      stage ^= 1;
     }
-#undef DG_LOAD_STAGE
-#undef DG_STORE_STAGE
 
     // ---- split-K: last arriving workgroup sums partials in split order ---------
     // The hand-off avoids device-scope fences (on a multi-XCD part they write back and
@@ -316,36 +417,27 @@ __global__ __launch_bounds__(64 * (BN / WN) * (BM / WM)) void gemm_fp8_kernel(Ge
       }
       __syncthreads();
       if (!s_flag) continue;
-      const float* base = p.ws + (int64_t)t.tile_id * p.splits * (int64_t)(kVals * NT);
-      // fixed order: sum = p_0 + p_1 + ... + p_{S-1}; this workgroup's own partial comes from registers
-      v4f red[C::kFragN][C::kFragM];
+      // fixed order acc = p_0 + p_1 + ... + p_{S-1}, every partial (this workgroup's own
+      // included) read back from the workspace, so the sum does not depend on who arrived last.
+      // One n-fragment row of values is loaded together before it is added (loads in flight).
+      const float* base = p.ws + (int64_t)t.tile_id * p.splits * (int64_t)(kVals * NT) + tid;
       for (int s = 0; s < p.splits; ++s) {
-        v4f v[C::kFragN][C::kFragM];
-        if (s == t.split) {
+        const float* src = base + (int64_t)s * (kVals * NT);
 #pragma unroll
-          for (int i = 0; i < C::kFragN; ++i)
+        for (int i = 0; i < C::kFragN; ++i) {
+          float v[C::kFragM][4];
 #pragma unroll
-            for (int j = 0; j < C::kFragM; ++j) v[i][j] = acc[i][j];
-        } else {
-          const float* src = base + (int64_t)s * (kVals * NT) + tid;
+          for (int j = 0; j < C::kFragM; ++j)
 #pragma unroll
-          for (int i = 0; i < C::kFragN; ++i)
+            for (int r = 0; r < 4; ++r)
+              v[j][r] = __hip_atomic_load(src + ((i * C::kFragM + j) * 4 + r) * NT, __ATOMIC_RELAXED,
+                                          __HIP_MEMORY_SCOPE_AGENT);
 #pragma unroll
-            for (int j = 0; j < C::kFragM; ++j)
+          for (int j = 0; j < C::kFragM; ++j)
 #pragma unroll
-              for (int r = 0; r < 4; ++r)
-                v[i][j][r] = __hip_atomic_load(src + ((i * C::kFragM + j) * 4 + r) * NT, __ATOMIC_RELAXED,
-                                               __HIP_MEMORY_SCOPE_AGENT);
+            for (int r = 0; r < 4; ++r) acc[i][j][r] = (s == 0) ? v[j][r] : acc[i][j][r] + v[j][r];
         }
-#pragma unroll
-        for (int i = 0; i < C::kFragN; ++i)
-#pragma unroll
-          for (int j = 0; j < C::kFragM; ++j) red[i][j] = (s == 0) ? v[i][j] : red[i][j] + v[i][j];
       }
-#pragma unroll
-      for (int i = 0; i < C::kFragN; ++i)
-#pragma unroll
-        for (int j = 0; j < C::kFragM; ++j) acc[i][j] = red[i][j];
       if (tid == 0)   // leave the counter zeroed for the next call
         __hip_atomic_store(p.counters + t.tile_id, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
@@ -355,12 +447,12 @@ __global__ __launch_bounds__(64 * (BN / WN) * (BM / WM)) void gemm_fp8_kernel(Ge
     const bool vec_ok = (p.n & 3) == 0;
 #pragma unroll
     for (int j = 0; j < C::kFragM; ++j) {
-      const int mrow = m0 + wave_m * WM + 16 * j + l16;
+      const int mrow = m0 + wm0 + 16 * j + l16;
       if (mrow >= t.m_valid) continue;
       uint16_t* drow = d_g + (int64_t)mrow * p.n;
 #pragma unroll
       for (int i = 0; i < C::kFragN; ++i) {
-        const int ncol = n0 + wave_n * WN + 16 * i + 4 * g4;
+        const int ncol = n0 + wn0 + 16 * i + 4 * g4;
         const uint16_t h0 = f32_to_bf16_rne(acc[i][j][0]);
         const uint16_t h1 = f32_to_bf16_rne(acc[i][j][1]);
         const uint16_t h2 = f32_to_bf16_rne(acc[i][j][2]);
@@ -389,20 +481,29 @@ struct LaunchInfo {
   const void* fn;
 };
 
-template <int BN, int BM, int WN, int WM, int LAYOUT>
+template <class C, int LAYOUT>
 static LaunchInfo info() {
-  return LaunchInfo{BN, BM, TileCfg<BN, BM, WN, WM>::kThreads,
-                    reinterpret_cast<const void*>(&gemm_fp8_kernel<BN, BM, WN, WM, LAYOUT>)};
+  void (*fn)(GemmParams) = gemm_fp8_kernel<C, LAYOUT>;
+  return LaunchInfo{C::BN, C::BM, C::kThreads, reinterpret_cast<const void*>(fn)};
 }
 
-// Tile configurations (BN x BM, wave tile WN x WM).
-enum Cfg : int { kCfgLarge = 0, kCfgSmallM = 1, kNumCfg = 2 };
+// Tile configurations: BN x BM workgroup tile, WN x WM wave tile, LDS stages.
+//  kCfgLarge   256x128, 8 waves of 64x64, 3 stages (~147 KB LDS): compute-bound shapes.
+//  kCfgRows128 the same tile for the contiguous layout (the expert changes every 128 rows).
+//  kCfgDecode  128xBM (BM = 64 or 128), 4 waves, 4 stages: small-m, HBM-bound shapes.
+enum CfgId : int { kCfgLarge = 0, kCfgRows128 = 1, kCfgDecode64 = 2, kCfgDecode128 = 3, kNumCfg = 4 };
+using CfgLarge = Cfg<256, 128, 64, 64, 3>;
+using CfgRows128 = Cfg<256, 128, 64, 64, 3>;
+using CfgDecode64 = Cfg<128, 64, 64, 32, 4>;
+using CfgDecode128 = Cfg<128, 128, 64, 64, 3>;
 
 template <int LAYOUT>
 static LaunchInfo cfg_info(int cfg) {
   switch (cfg) {
-    case kCfgSmallM: return info<128, 64, 64, 32, LAYOUT>();
-    default: return info<128, 128, 64, 64, LAYOUT>();
+    case kCfgRows128: return info<CfgRows128, LAYOUT>();
+    case kCfgDecode64: return info<CfgDecode64, LAYOUT>();
+    case kCfgDecode128: return info<CfgDecode128, LAYOUT>();
+    default: return info<CfgLarge, LAYOUT>();
   }
 }
 
@@ -415,23 +516,30 @@ static int occupancy(const LaunchInfo& li) {
 
 struct Plan {
   int cfg;
+  int bn, bm;
   int splits;
   int kb_per_split;
   int tiles_m, tiles_n;
   size_t ws_bytes;   // needed workspace for this plan (0 when splits == 1)
 };
 
-// Pick the tile config and the K split for a problem with `tiles` output tiles per group.
-static Plan make_plan(int64_t m, int64_t n, int64_t k, int64_t groups, int num_cus, bool allow_split) {
+// Pick the tile config and the K split.  `groups` multiplies the tile count (masked layout).
+static Plan make_plan(int layout, int64_t m, int64_t n, int64_t k, int64_t groups, int num_cus, bool allow_split) {
   Plan pl{};
-  pl.cfg = (m <= 64) ? kCfgSmallM : kCfgLarge;
-  const int bn = 128, bm = (pl.cfg == kCfgSmallM) ? 64 : 128;
-  pl.tiles_m = (int)((m + bm - 1) / bm);
-  pl.tiles_n = (int)((n + bn - 1) / bn);
+  if (layout == kContiguous) pl.cfg = kCfgRows128;
+  else if (m <= 64) pl.cfg = kCfgDecode64;
+  else if (m <= 128) pl.cfg = kCfgDecode128;
+  else pl.cfg = kCfgLarge;
+  const LaunchInfo li = cfg_info<kDense>(pl.cfg);
+  pl.bn = li.bn;
+  pl.bm = li.bm;
+  pl.tiles_m = (int)((m + pl.bm - 1) / pl.bm);
+  pl.tiles_n = (int)((n + pl.bn - 1) / pl.bn);
   const int kb_total = (int)(k / kGroup);
   const int64_t tiles = (int64_t)pl.tiles_m * pl.tiles_n * groups;
   pl.splits = 1;
-  if (allow_split && tiles < num_cus) {
+  const bool decode_cfg = pl.cfg == kCfgDecode64 || pl.cfg == kCfgDecode128;
+  if (allow_split && decode_cfg && tiles < num_cus) {
     int want = (int)((num_cus + tiles - 1) / tiles);
     const int max_split = kb_total / 4 > 0 ? kb_total / 4 : 1;   // keep >= 4 K blocks per split
     if (want > max_split) want = max_split;
@@ -442,28 +550,28 @@ static Plan make_plan(int64_t m, int64_t n, int64_t k, int64_t groups, int num_c
   pl.ws_bytes = 0;
   if (pl.splits > 1) {
     const size_t counters = ((size_t)tiles * 4 + 255) & ~(size_t)255;
-    pl.ws_bytes = counters + (size_t)tiles * pl.splits * (size_t)bn * bm * 4;
+    pl.ws_bytes = counters + (size_t)tiles * pl.splits * (size_t)pl.bn * pl.bm * 4;
   }
   return pl;
 }
 
 void gemm_config_name(int layout, int64_t m, int64_t n, int64_t k, int64_t groups, int num_cus, char* buf,
                       size_t len) {
-  const Plan pl = make_plan(m, n, k, layout == kMasked ? groups : 1, num_cus, layout != kContiguous);
+  const Plan pl = make_plan(layout, m, n, k, layout == kMasked ? groups : 1, num_cus, layout != kContiguous);
   const LaunchInfo li = cfg_info<kDense>(pl.cfg);
-  const int waves = li.threads / 64;
-  snprintf(buf, len, "%dx%d/%dwaves/split%d", li.bn, li.bm, waves, pl.splits);
+  snprintf(buf, len, "%dx%d/%dwaves/split%d", li.bn, li.bm, li.threads / 64, pl.splits);
 }
 
 size_t gemm_workspace_size(int64_t m, int64_t n, int64_t k, int64_t groups, int num_cus) {
-  return make_plan(m, n, k, groups, num_cus, true).ws_bytes;
+  const int layout = groups > 1 ? kMasked : kDense;
+  return make_plan(layout, m, n, k, groups, num_cus, true).ws_bytes;
 }
 
 template <int LAYOUT>
 static int launch_layout(GemmParams p, const Plan& pl, hipStream_t stream, int num_cus) {
   const LaunchInfo li = cfg_info<LAYOUT>(pl.cfg);
   const int occ = occupancy(li);
-  int64_t items = (int64_t)pl.tiles_m * pl.tiles_n * (LAYOUT == kContiguous ? 1 : p.num_groups) * pl.splits;
+  const int64_t items = (int64_t)pl.tiles_m * pl.tiles_n * (LAYOUT == kContiguous ? 1 : p.num_groups) * pl.splits;
   if (items > 0x7fffffffLL) return set_error(kUnsupported, "gemm: too many work items");
   int64_t grid = (int64_t)num_cus * occ;
   if (grid > items) grid = items;
@@ -480,9 +588,11 @@ int launch_gemm(int layout, const uint8_t* a, const float* sa, int64_t ld_sa, co
   if (n * k > 0x7fffffffLL || m * k > 0x7fffffffLL)
     return set_error(kUnsupported, "gemm: one group's operand must be < 2^31 bytes (m=%lld n=%lld k=%lld)",
                      (long long)m, (long long)n, (long long)k);
+  if (layout == kMasked && groups > 1024) return set_error(kUnsupported, "masked gemm: at most 1024 groups");
+  const int64_t tile_groups = layout == kMasked ? groups : 1;
   const bool can_split = (layout != kContiguous) && ws != nullptr;
-  Plan pl = make_plan(m, n, k, layout == kMasked ? groups : 1, num_cus, can_split);
-  if (pl.splits > 1 && ws_bytes < pl.ws_bytes) pl = make_plan(m, n, k, layout == kMasked ? groups : 1, num_cus, false);
+  Plan pl = make_plan(layout, m, n, k, tile_groups, num_cus, can_split);
+  if (pl.splits > 1 && ws_bytes < pl.ws_bytes) pl = make_plan(layout, m, n, k, tile_groups, num_cus, false);
 
   GemmParams p{};
   p.a = a; p.sa = sa; p.b = b; p.sb = sb; p.d = d;
@@ -500,12 +610,11 @@ int launch_gemm(int layout, const uint8_t* a, const float* sa, int64_t ld_sa, co
   p.sb_gstride = (int64_t)p.nb128 * p.kb_total;
   p.d_gstride = m * n;
   if (pl.splits > 1) {
-    const int64_t tiles = (int64_t)pl.tiles_m * pl.tiles_n * p.num_groups;
+    const int64_t tiles = (int64_t)pl.tiles_m * pl.tiles_n * tile_groups;
     const size_t counters = ((size_t)tiles * 4 + 255) & ~(size_t)255;
     p.counters = static_cast<unsigned*>(ws);
     p.ws = reinterpret_cast<float*>(static_cast<uint8_t*>(ws) + counters);
   }
-  if (layout == kMasked && groups > 1024) return set_error(kUnsupported, "masked gemm: at most 1024 groups");
   switch (layout) {
     case kContiguous: return launch_layout<kContiguous>(p, pl, stream, num_cus);
     case kMasked: return launch_layout<kMasked>(p, pl, stream, num_cus);
