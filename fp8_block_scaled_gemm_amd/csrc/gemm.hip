@@ -39,44 +39,11 @@
 #include <cstdio>
 #include <type_traits>
 
-#include "common.hpp"
+#include "gemm_common.hpp"
 
 namespace dg {
 
-enum Layout : int { kDense = 0, kContiguous = 1, kMasked = 2 };
-
-struct GemmParams {
-  const uint8_t* a;
-  const float* sa;
-  const uint8_t* b;
-  const float* sb;
-  uint16_t* d;
-  const int32_t* m_indices;   // contiguous: expert per row
-  const int32_t* masked_m;    // masked: valid rows per group
-  float* ws;                  // split-K partials
-  unsigned* counters;         // split-K arrival counters, one per tile
-  int64_t ld_sa;
-  int64_t a_gstride, sa_gstride, b_gstride, sb_gstride, d_gstride;   // per-group strides (elements)
-  int m;            // rows per group (dense: M, contiguous: M_total, masked: M_max)
-  int n, k;
-  int num_groups;
-  int kb_total;     // k / 128
-  int tiles_m;      // ceil(m / BM)
-  int tiles_n;      // ceil(n / BN)
-  int splits;       // K splits (1 = none)
-  int kb_per_split;
-  int nb128;        // ceil(n / 128): weight-scale rows per group
-};
-
-typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) void lds_void;
-// Buffer resource word 3 for raw (untyped, stride 0) buffer accesses on gfx9-family parts.
-constexpr int kBufferWord3 = 0x00020000;
-
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int64_t bytes) {
-  const int n = bytes > 0x7fffffffLL ? 0x7fffffff : (int)bytes;
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, n, kBufferWord3);
-}
 
 // LDS DMA: every active lane copies 16 (4) bytes from rsrc + voff + soff into lds + lane * 16 (4)
 // (buffer_load_dword{,x4} ... lds; out-of-range offsets read zeros).
@@ -161,7 +128,9 @@ __global__ __launch_bounds__(C::kThreads) void gemm_fp8_kernel(GemmParams p) {
   __shared__ __attribute__((aligned(1024))) uint8_t st2[S > 2 ? C::kStageBytes : 16];
   __shared__ __attribute__((aligned(1024))) uint8_t st3[S > 3 ? C::kStageBytes : 16];
   __shared__ int s_prefix[LAYOUT == kMasked ? 1025 : 1];
+  __shared__ int s_scan[LAYOUT == kMasked ? 256 : 1];
   __shared__ int s_flag;
+  static_assert(NT >= 256, "the masked-layout prefix needs 256 threads");
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -177,17 +146,7 @@ __global__ __launch_bounds__(C::kThreads) void gemm_fp8_kernel(GemmParams p) {
   int total_items;
   if constexpr (LAYOUT == kMasked) {
     // prefix over groups of the number of (m-block, n-block) tiles, from device counts
-    if (tid == 0) {
-      int acc = 0;
-      s_prefix[0] = 0;
-      for (int g = 0; g < p.num_groups; ++g) {
-        int mv = p.masked_m[g];
-        mv = mv < 0 ? 0 : (mv > p.m ? p.m : mv);
-        acc += ((mv + C::BM - 1) / C::BM) * p.tiles_n;
-        s_prefix[g + 1] = acc;
-      }
-    }
-    __syncthreads();
+    masked_item_prefix(p.masked_m, p.num_groups, p.m, C::BM, p.tiles_n, s_prefix, s_scan);
     total_items = s_prefix[p.num_groups] * p.splits;
   } else {
     // contiguous: the expert comes from m_indices, not from the item index
@@ -206,8 +165,7 @@ __global__ __launch_bounds__(C::kThreads) void gemm_fp8_kernel(GemmParams p) {
     t.split = item % p.splits;
     int rest = item / p.splits;
     if constexpr (LAYOUT == kMasked) {
-      int g = 0;
-      while (s_prefix[g + 1] <= rest) ++g;
+      const int g = masked_group_of(s_prefix, p.num_groups, rest);
       rest -= s_prefix[g];
       const int mblocks = (s_prefix[g + 1] - s_prefix[g]) / p.tiles_n;
       t.g = g;
@@ -398,16 +356,16 @@ __global__ __launch_bounds__(C::kThreads) void gemm_fp8_kernel(GemmParams p) {
     // arrival counter is bumped, and the last workgroup reads them back with
     // agent-scope loads, which miss in its own (non-coherent) L2.
     if (p.splits > 1) {
-      constexpr int kVals = C::kFragN * C::kFragM * 4;
-      float* mine = p.ws + ((int64_t)t.tile_id * p.splits + t.split) * (int64_t)(kVals * NT);
+      // partial layout: [fragment][thread][4] - 16 bytes per thread and fragment (coalesced)
+      constexpr int kFrags = C::kFragN * C::kFragM;
+      constexpr int kSplitBytes = kFrags * NT * 16;
+      float* ws_tile = p.ws + (int64_t)t.tile_id * p.splits * (int64_t)(kSplitBytes / 4);
+      const __amdgpu_buffer_rsrc_t rs_ws = make_rsrc(ws_tile, (int64_t)p.splits * kSplitBytes);
+      const int own = t.split * kSplitBytes + tid * 16;
 #pragma unroll
-      for (int i = 0; i < C::kFragN; ++i)
-#pragma unroll
-        for (int j = 0; j < C::kFragM; ++j)
-#pragma unroll
-          for (int r = 0; r < 4; ++r)
-            __hip_atomic_store(mine + ((i * C::kFragM + j) * 4 + r) * NT + tid, acc[i][j][r], __ATOMIC_RELAXED,
-                               __HIP_MEMORY_SCOPE_AGENT);
+      for (int f = 0; f < kFrags; ++f)
+        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, acc[f / C::kFragM][f % C::kFragM]), rs_ws,
+                                               own + f * NT * 16, 0, kCpolSc1);
       __builtin_amdgcn_s_waitcnt(0);   // every partial store of this thread has completed
       __syncthreads();
       if (tid == 0) {
@@ -419,23 +377,24 @@ __global__ __launch_bounds__(C::kThreads) void gemm_fp8_kernel(GemmParams p) {
       if (!s_flag) continue;
       // fixed order acc = p_0 + p_1 + ... + p_{S-1}, every partial (this workgroup's own
       // included) read back from the workspace, so the sum does not depend on who arrived last.
-      // One n-fragment row of values is loaded together before it is added (loads in flight).
-      const float* base = p.ws + (int64_t)t.tile_id * p.splits * (int64_t)(kVals * NT) + tid;
-      for (int s = 0; s < p.splits; ++s) {
-        const float* src = base + (int64_t)s * (kVals * NT);
+      // Up to kBatch splits are loaded together (all in flight) before they are added.
+      constexpr int kBatch = kFrags >= 32 ? 1 : 32 / kFrags;
+      for (int s0 = 0; s0 < p.splits; s0 += kBatch) {
+        v4f v[kBatch][kFrags];
 #pragma unroll
-        for (int i = 0; i < C::kFragN; ++i) {
-          float v[C::kFragM][4];
+        for (int u = 0; u < kBatch; ++u) {
+          const int sp = s0 + u < p.splits ? s0 + u : s0;
 #pragma unroll
-          for (int j = 0; j < C::kFragM; ++j)
+          for (int f = 0; f < kFrags; ++f)
+            v[u][f] = __builtin_bit_cast(v4f, __builtin_amdgcn_raw_buffer_load_b128(
+                                                  rs_ws, sp * kSplitBytes + tid * 16 + f * NT * 16, 0, kCpolSc1));
+        }
 #pragma unroll
-            for (int r = 0; r < 4; ++r)
-              v[j][r] = __hip_atomic_load(src + ((i * C::kFragM + j) * 4 + r) * NT, __ATOMIC_RELAXED,
-                                          __HIP_MEMORY_SCOPE_AGENT);
+        for (int u = 0; u < kBatch; ++u) {
+          if (s0 + u >= p.splits) break;
 #pragma unroll
-          for (int j = 0; j < C::kFragM; ++j)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) acc[i][j][r] = (s == 0) ? v[j][r] : acc[i][j][r] + v[j][r];
+          for (int f = 0; f < kFrags; ++f)
+            acc[f / C::kFragM][f % C::kFragM] = (s0 + u == 0) ? v[u][f] : acc[f / C::kFragM][f % C::kFragM] + v[u][f];
         }
       }
       if (tid == 0)   // leave the counter zeroed for the next call
@@ -477,32 +436,40 @@ __global__ __launch_bounds__(C::kThreads) void gemm_fp8_kernel(GemmParams p) {
 // Host side: tile configurations, occupancy, split-K choice and launch.
 // ---------------------------------------------------------------------------
 struct LaunchInfo {
-  int bn, bm, threads;
+  int bn, bm, threads, stages;
   const void* fn;
 };
 
 template <class C, int LAYOUT>
 static LaunchInfo info() {
   void (*fn)(GemmParams) = gemm_fp8_kernel<C, LAYOUT>;
-  return LaunchInfo{C::BN, C::BM, C::kThreads, reinterpret_cast<const void*>(fn)};
+  return LaunchInfo{C::BN, C::BM, C::kThreads, C::STAGES, reinterpret_cast<const void*>(fn)};
 }
 
 // Tile configurations: BN x BM workgroup tile, WN x WM wave tile, LDS stages.
 //  kCfgLarge   256x128, 8 waves of 64x64, 3 stages (~147 KB LDS): compute-bound shapes.
 //  kCfgRows128 the same tile for the contiguous layout (the expert changes every 128 rows).
-//  kCfgDecode  128xBM (BM = 64 or 128), 4 waves, 4 stages: small-m, HBM-bound shapes.
-enum CfgId : int { kCfgLarge = 0, kCfgRows128 = 1, kCfgDecode64 = 2, kCfgDecode128 = 3, kNumCfg = 4 };
+//  kCfgWide    256x192, 8 waves of 128x48, 2 stages (~114 KB LDS): 1.5x the work per tile and
+//              ~1/6 less operand traffic per flop than kCfgLarge; chosen when it needs fewer
+//              rounds of the persistent grid (wave quantisation decides most shapes).
+//  kCfgDec*    m <= 64 / m <= 128 rows: 64 weight rows x 64 or 128 activation rows, 4 waves,
+//              two workgroups per CU: HBM-bound shapes.  (Measured against 128-row weight tiles
+//              on all twelve M = 64 / 128 DeepSeek-V3 shapes: the 64-row tile, with K split to
+//              fill the grid, is faster on every one.)
+enum CfgId : int { kCfgLarge = 0, kCfgRows128, kCfgWide, kCfgDec64, kCfgDec128, kNumCfg };
 using CfgLarge = Cfg<256, 128, 64, 64, 3>;
 using CfgRows128 = Cfg<256, 128, 64, 64, 3>;
-using CfgDecode64 = Cfg<128, 64, 64, 32, 4>;
-using CfgDecode128 = Cfg<128, 128, 64, 64, 3>;
+using CfgWide = Cfg<256, 192, 128, 48, 2>;
+using CfgDec64 = Cfg<64, 64, 32, 32, 4>;
+using CfgDec128 = Cfg<64, 128, 32, 64, 3>;
 
 template <int LAYOUT>
 static LaunchInfo cfg_info(int cfg) {
   switch (cfg) {
+    case kCfgWide: return info<CfgWide, LAYOUT>();
+    case kCfgDec64: return info<CfgDec64, LAYOUT>();
+    case kCfgDec128: return info<CfgDec128, LAYOUT>();
     case kCfgRows128: return info<CfgRows128, LAYOUT>();
-    case kCfgDecode64: return info<CfgDecode64, LAYOUT>();
-    case kCfgDecode128: return info<CfgDecode128, LAYOUT>();
     default: return info<CfgLarge, LAYOUT>();
   }
 }
@@ -520,38 +487,108 @@ struct Plan {
   int splits;
   int kb_per_split;
   int tiles_m, tiles_n;
+  int64_t tiles;     // output tiles (one split-K counter each)
   size_t ws_bytes;   // needed workspace for this plan (0 when splits == 1)
 };
 
-// Pick the tile config and the K split.  `groups` multiplies the tile count (masked layout).
-static Plan make_plan(int layout, int64_t m, int64_t n, int64_t k, int64_t groups, int num_cus, bool allow_split) {
-  Plan pl{};
-  if (layout == kContiguous) pl.cfg = kCfgRows128;
-  else if (m <= 64) pl.cfg = kCfgDecode64;
-  else if (m <= 128) pl.cfg = kCfgDecode128;
-  else pl.cfg = kCfgLarge;
+static void finish_plan(Plan& pl, int64_t m, int64_t n, int64_t groups) {
   const LaunchInfo li = cfg_info<kDense>(pl.cfg);
   pl.bn = li.bn;
   pl.bm = li.bm;
-  pl.tiles_m = (int)((m + pl.bm - 1) / pl.bm);
-  pl.tiles_n = (int)((n + pl.bn - 1) / pl.bn);
+  pl.tiles_m = (int)((m + li.bm - 1) / li.bm);
+  pl.tiles_n = (int)((n + li.bn - 1) / li.bn);
+  pl.tiles = (int64_t)pl.tiles_m * pl.tiles_n * groups;
+  pl.ws_bytes = 0;
+  if (pl.splits > 1) {
+    const size_t counters = ((size_t)pl.tiles * 4 + 255) & ~(size_t)255;
+    pl.ws_bytes = counters + (size_t)pl.tiles * pl.splits * (size_t)li.bn * li.bm * 4;
+  }
+}
+
+// Large-m tile choice: estimated time = rounds of the persistent grid x time per tile round.  A
+// 256x192 tile round takes ~1.36x a 256x128 round (1.5x the MFMA work, less operand traffic per
+// flop: measured on 16384x7168x16384), so it wins where it saves a round, e.g. 4096x2112 (198
+// tiles, one round, vs 288) or 4096x32768 (11 rounds vs 16).
+static int choose_large(int64_t m, int64_t n, int64_t groups, int num_cus) {
+  auto rounds = [&](int bn, int bm) {
+    const int64_t tiles = ((m + bm - 1) / bm) * ((n + bn - 1) / bn) * groups;
+    return (tiles + num_cus - 1) / num_cus;   // both configurations run one workgroup per CU
+  };
+  const double t_large = (double)rounds(CfgLarge::BN, CfgLarge::BM);
+  const double t_wide = 1.36 * (double)rounds(CfgWide::BN, CfgWide::BM);
+  return t_wide < t_large ? kCfgWide : kCfgLarge;
+}
+
+// Few-row plan (m <= 128 per group): the K split from a model of the streaming regime, fitted to
+// timings of every split on MI355X.  Work items spread evenly over the CUs; a CU running c
+// workgroups keeps c * (STAGES - 1) stages of both operand tiles in flight, each taking ~1.5 us
+// to arrive; the whole grid is further bound by HBM (~5 TB/s for the weights, read once) and by
+// L2-to-CU delivery (~8 TB/s for both tiles: the activation tile is re-read by every weight
+// tile); a split's hand-off costs ~2 us plus the last workgroup's read of every partial at
+// ~100 GB/s.  Returns the estimated time in microseconds.
+static double decode_estimate(const LaunchInfo& li, int occ, int64_t m, int64_t n, int kb_total, int64_t groups,
+                              int num_cus, int splits, int kbps) {
+  const int64_t tiles = ((m + li.bm - 1) / li.bm) * ((n + li.bn - 1) / li.bn) * groups;
+  const int64_t items = tiles * splits;
+  const int64_t per_cu = (items + num_cus - 1) / num_cus;
+  const double conc = (double)(per_cu < occ ? per_cu : occ);
+  const double stage = (double)(li.bn + li.bm) * kGroup;
+  const double rate = conc * (li.stages - 1) * stage / 1.5;   // bytes per us
+  double t = (double)per_cu * stage * kbps / rate;
+  const double l2 = (double)items * stage * kbps / 8.0e6;
+  const double hbm = (double)tiles * li.bn * kGroup * kb_total / 5.0e6;
+  if (t < l2) t = l2;
+  if (t < hbm) t = hbm;
+  if (splits > 1) t += 2.0 + (double)splits * li.bn * li.bm * 4 / 1.0e5;
+  return t;
+}
+
+static Plan make_decode_plan(int64_t m, int64_t n, int64_t k, int64_t groups, int num_cus, bool allow_split) {
   const int kb_total = (int)(k / kGroup);
-  const int64_t tiles = (int64_t)pl.tiles_m * pl.tiles_n * groups;
+  Plan pl{};
+  pl.cfg = m <= 64 ? kCfgDec64 : kCfgDec128;
   pl.splits = 1;
-  const bool decode_cfg = pl.cfg == kCfgDecode64 || pl.cfg == kCfgDecode128;
-  if (allow_split && decode_cfg && tiles < num_cus) {
-    int want = (int)((num_cus + tiles - 1) / tiles);
+  pl.kb_per_split = kb_total;
+  const LaunchInfo li = cfg_info<kDense>(pl.cfg);
+  const int occ = occupancy(li);
+  int max_split = kb_total / 2 < kMaxSplits ? kb_total / 2 : kMaxSplits;
+  if (!allow_split || max_split < 1) max_split = 1;
+  double best_t = 1e30;
+  for (int want = 1; want <= max_split; ++want) {
+    const int kbps = (kb_total + want - 1) / want;
+    const int splits = (kb_total + kbps - 1) / kbps;
+    if (splits != want) continue;   // the same split as a smaller request
+    const double t = decode_estimate(li, occ, m, n, kb_total, groups, num_cus, splits, kbps);
+    if (t < best_t) {
+      best_t = t;
+      pl.splits = splits;
+      pl.kb_per_split = kbps;
+    }
+  }
+  finish_plan(pl, m, n, groups);
+  return pl;
+}
+
+// Pick the tile config and the K split.  `groups` multiplies the tile count (masked layout).
+static Plan make_plan(int layout, int64_t m, int64_t n, int64_t k, int64_t groups, int num_cus, bool allow_split) {
+  if (layout != kContiguous && m <= 128) return make_decode_plan(m, n, k, groups, num_cus, allow_split);
+  Plan pl{};
+  pl.cfg = layout == kContiguous ? kCfgRows128 : choose_large(m, n, groups, num_cus);
+  const LaunchInfo li = cfg_info<kDense>(pl.cfg);
+  const int kb_total = (int)(k / kGroup);
+  pl.splits = 1;
+  // few tiles and a long K (e.g. 256 x 512 x 8192): split K so that every CU gets work
+  const int64_t tiles = ((m + li.bm - 1) / li.bm) * ((n + li.bn - 1) / li.bn) * groups;
+  if (allow_split && 2 * tiles <= num_cus) {
+    int want = (int)(num_cus / tiles);
     const int max_split = kb_total / 4 > 0 ? kb_total / 4 : 1;   // keep >= 4 K blocks per split
     if (want > max_split) want = max_split;
+    if (want > kMaxSplits) want = kMaxSplits;
     if (want > 1) pl.splits = want;
   }
   pl.kb_per_split = (kb_total + pl.splits - 1) / pl.splits;
   pl.splits = (kb_total + pl.kb_per_split - 1) / pl.kb_per_split;   // no empty split
-  pl.ws_bytes = 0;
-  if (pl.splits > 1) {
-    const size_t counters = ((size_t)tiles * 4 + 255) & ~(size_t)255;
-    pl.ws_bytes = counters + (size_t)tiles * pl.splits * (size_t)pl.bn * pl.bm * 4;
-  }
+  finish_plan(pl, m, n, groups);
   return pl;
 }
 
@@ -610,8 +647,7 @@ int launch_gemm(int layout, const uint8_t* a, const float* sa, int64_t ld_sa, co
   p.sb_gstride = (int64_t)p.nb128 * p.kb_total;
   p.d_gstride = m * n;
   if (pl.splits > 1) {
-    const int64_t tiles = (int64_t)pl.tiles_m * pl.tiles_n * tile_groups;
-    const size_t counters = ((size_t)tiles * 4 + 255) & ~(size_t)255;
+    const size_t counters = ((size_t)pl.tiles * 4 + 255) & ~(size_t)255;
     p.counters = static_cast<unsigned*>(ws);
     p.ws = reinterpret_cast<float*>(static_cast<uint8_t*>(ws) + counters);
   }
