@@ -1,17 +1,27 @@
 """Benchmark of the FP8 block-scaled GEMM hot path on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload dense_v3|small|contiguous|masked|
-                     large_dense|zipf] [--no-cpu-baseline] [--cpu-seconds S]
+                     large_dense|zipf] [--no-cpu-baseline] [--cpu-seconds S] [--eager]
+    python bench.py --copy-calibration      # counter calibration: one plain 1 GiB device copy
 
 One step is one pass of the whole hot path over one batch of synthetic input:
 weight quantization (128x128 blocks) of every weight matrix of the workload,
 then, per GEMM shape, activation quantization (1x128 groups) followed by the
 FP8 GEMM with promoted accumulation - every kernel of the library, in the order
-a training forward pass runs them.  Inputs are resident in HBM before timing.
+a forward pass runs them.  Inputs are resident in HBM before timing.
+
+Timing: the step is captured once as a HIP graph; the timed region is K graph
+replays on one stream, bracketed by device synchronisation (so microsecond
+kernels are not measured at the host's launch rate).  Per-kernel durations come
+from a second pass of K eager steps on the same stream with a HIP event pair
+around every launch; a bounded spin kernel ahead of each pass keeps the device
+busy while the host enqueues it, so every event pair brackets only its kernel.
+
 Prints ONE JSON line: the workload's GEMM FP8 TFLOP/s over the whole step, plus
 per-shape GEMM TFLOP/s and HBM GB/s, the roofline of the dominant GEMM kernel
-(timed with HIP events on the launch stream) and the CPU oracle's throughput on
-a bounded sample of the same workload.
+(with the HBM traffic that rocprofv3 counters measured for it, when the committed
+counter summary matches the kernel source) and the CPU oracle's throughput on a
+bounded sample of the same workload.
 
 Workloads: DeepSeek-V3/R1 inference shapes (prefill and decode, no tensor
 parallelism - the pages' own benchmark set, 机器之心 DeepGEMM report,
@@ -44,6 +54,11 @@ def parse():
                     choices=["dense_v3", "small", "contiguous", "masked", "large_dense", "zipf"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target CPU work of the oracle sample")
+    ap.add_argument("--eager", action="store_true", help="time eager launches instead of graph replays")
+    ap.add_argument("--spin-ms", type=float, default=20.0,
+                    help="device spin before each per-kernel timing pass (covers the host's enqueue time)")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain 1 GiB device copy (calibrates the FETCH_SIZE / WRITE_SIZE counters)")
     return ap.parse_args()
 
 
@@ -267,6 +282,43 @@ def cpu_baseline(workload, seconds):
 
 # ---------------------------------------------------------------------------
 
+def source_digest():
+    """sha256 of the GEMM kernel source: traffic counters are only valid for the kernel they measured."""
+    import hashlib
+    h = hashlib.sha256()
+    for f in ("gemm.hip", "gemm_common.hpp", "common.hpp"):
+        with open(os.path.join(ROOT, "fp8_block_scaled_gemm_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(workload, kernel, launches_bytes):
+    """HBM bytes per launch of `kernel` from the committed rocprofv3 counter summary, scaled by the
+    copy-kernel calibration; None if there is none for this workload/kernel or the source changed."""
+    path = os.path.join(ROOT, "profiles", "traffic_counters.json")
+    try:
+        with open(path) as fh:
+            data = json.load(fh)
+    except (OSError, ValueError):
+        return None
+    rec = data.get(workload, {}).get(kernel)
+    if not rec or rec.get("source_sha") != source_digest():
+        return None
+    return {"bytes_per_launch": rec["hbm_bytes_per_launch"], "algorithmic_bytes_per_launch": launches_bytes,
+            "ratio": round(rec["hbm_bytes_per_launch"] / launches_bytes, 3), "source": "profiles/traffic_counters.json"}
+
+
+def copy_calibration(torch, dev, nbytes=1 << 30, reps=5):
+    """A plain device copy of known size, profiled with the FETCH_SIZE / WRITE_SIZE counters to scale
+    them to bytes (one launch reads and writes nbytes)."""
+    src = torch.empty(nbytes, dtype=torch.uint8, device=dev).fill_(1)
+    dst = torch.empty_like(src)
+    for _ in range(reps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes": nbytes, "launches": reps}), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -280,42 +332,76 @@ def main():
         print("bench.py: no GPU visible", file=sys.stderr)
         sys.exit(1)
     dev = torch.device("cuda", 0)
+    if args.copy_calibration:
+        copy_calibration(torch, dev)
+        return
     dg.lib()
     ops, desc = build_workload(args.workload, torch, dg, dev)
     torch.cuda.synchronize()
     print(f"[bench] workload {args.workload}: {len(ops)} ops per step", file=sys.stderr, flush=True)
 
-    n = len(ops)
+    def step():
+        for op in ops:
+            op.launch()
 
-    def step(record):
-        if record:
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    print("[bench] warmup done", file=sys.stderr, flush=True)
+
+    # ---- timed region: K steps, each one replay of the step captured as a HIP graph (no host
+    # launch gaps between the kernels); wall clock bracketed by device synchronisation --------------
+    stream = torch.cuda.Stream()
+    graph = None
+    if not args.eager:
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph, stream=stream):
+            step()
+        graph.replay()
+        torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    with torch.cuda.stream(stream):
+        ev0.record()
+        for _ in range(args.steps):
+            if graph is not None:
+                graph.replay()
+            else:
+                step()
+        ev1.record()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_per_step = (t1 - t0) * 1e3 / args.steps
+    gpu_ms_per_step = ev0.elapsed_time(ev1) / args.steps
+    print(f"[bench] timed {args.steps} steps: {ms_per_step:.3f} ms/step (device {gpu_ms_per_step:.3f})",
+          file=sys.stderr, flush=True)
+
+    # ---- per-kernel durations: the same step run eagerly on the same stream with a HIP event pair
+    # around every launch.  A bounded spin kernel first keeps the device busy while the host enqueues
+    # the whole step, so each event pair brackets only its kernel (no host gap), in step order. -------
+    n = len(ops)
+    # spin length: the counter rate of the spin kernel, measured
+    cal0, cal1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    with torch.cuda.stream(stream):
+        cal0.record()
+        torch.cuda._sleep(1_000_000)
+        cal1.record()
+    torch.cuda.synchronize()
+    cycles_per_ms = 1_000_000 / max(cal0.elapsed_time(cal1), 1e-3)
+    spin_cycles = int(args.spin_ms * cycles_per_ms)
+    with torch.cuda.stream(stream):
+        for _ in range(args.steps):
             ev = [torch.cuda.Event(enable_timing=True) for _ in range(2 * n)]
+            torch.cuda._sleep(spin_cycles)
             for i, op in enumerate(ops):
                 ev[2 * i].record()
                 op.launch()
                 ev[2 * i + 1].record()
-            return ev
-        for op in ops:
-            op.launch()
-        return None
-
-    for _ in range(args.warmup):
-        step(False)
-    torch.cuda.synchronize()
-    print("[bench] warmup done", file=sys.stderr, flush=True)
-
-    all_ev = []
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for _ in range(args.steps):
-        all_ev.append(step(True))
-    torch.cuda.synchronize()
-    t1 = time.perf_counter()
-    ms_per_step = (t1 - t0) * 1e3 / args.steps
-    for ev in all_ev:
-        for i, op in enumerate(ops):
-            op.times.append(ev[2 * i].elapsed_time(ev[2 * i + 1]))
-    print(f"[bench] timed {args.steps} steps: {ms_per_step:.3f} ms/step", file=sys.stderr, flush=True)
+            torch.cuda.synchronize()
+            for i, op in enumerate(ops):
+                op.times.append(ev[2 * i].elapsed_time(ev[2 * i + 1]))
+    print("[bench] per-kernel timing done", file=sys.stderr, flush=True)
 
     gemm_flops = sum(op.flops for op in ops if op.kind == "gemm")
     value = gemm_flops / (ms_per_step * 1e-3) / 1e12
@@ -334,7 +420,7 @@ def main():
                                                   op.nbytes / (PEAK_HBM_GBS * 1e9)) / t, 4)})
 
     # dominant GEMM kernel: the kernel instance (tile configuration; the K split is a launch
-    # parameter of the same kernel) with the most event time over the timed region
+    # parameter of the same kernel) with the most device time per step
     by_cfg = {}
     for op in ops:
         if op.kind == "gemm":
@@ -349,10 +435,16 @@ def main():
         achieved, peak, unit = tot_f / tot_t / 1e12, PEAK_FP8_TFLOPS, "TFLOP/s"
     else:
         achieved, peak, unit = tot_b / tot_t / 1e9, PEAK_HBM_GBS, "GB/s"
+    kernel = f"gemm_fp8_kernel {dom_cfg}"
+    traffic = measured_traffic(args.workload, kernel, tot_b / launches)
     roofline = {"bound": "mfma" if mfma_bound else "hbm", "achieved": round(achieved, 1), "peak": peak,
-                "unit": unit, "frac": round(achieved / peak, 4), "traffic": None,
-                "kernel": f"gemm_fp8_kernel {dom_cfg}", "launches": launches,
+                "unit": unit, "frac": round(achieved / peak, 4),
+                "traffic": traffic["bytes_per_launch"] if traffic else None,
+                "traffic_detail": traffic,
+                "kernel": kernel, "launches": launches,
                 "avg_launch_us": round(tot_t / launches * 1e6, 2),
+                "algorithmic_bytes_per_launch": round(tot_b / launches),
+                "flops_per_launch": round(tot_f / launches),
                 "shapes": sorted({o.label for o in dom_ops})}
 
     quant = {}
@@ -375,6 +467,8 @@ def main():
            "scaling": "weak", "vs_baseline": None, "dtype": "fp8_e4m3", "data": "synthetic",
            "config": {"workload": args.workload, "description": desc, "gemms": len(shapes),
                       "step": "weight quantization (all weights) + per shape: activation quantization, FP8 GEMM",
+                      "timing": "eager" if graph is None else "hip graph replay per step",
+                      "device_ms_per_step": round(gpu_ms_per_step, 4),
                       "gemm_only_tflops": round(gemm_flops / (gemm_only_ms * 1e-3) / 1e12, 1),
                       "gemm_only_ms": round(gemm_only_ms, 4)},
            "roofline": roofline, "cpu_baseline": cpu, "quant": quant, "shapes": shapes}

@@ -519,7 +519,7 @@ static int choose_large(int64_t m, int64_t n, int64_t groups, int num_cus) {
   return t_wide < t_large ? kCfgWide : kCfgLarge;
 }
 
-// Few-row plan (m <= 128 per group): the K split from a model of the streaming regime, fitted to
+// Few-row plan (m <= 128 rows per group): the K split from a model of the streaming regime, fitted to
 // timings of every split on MI355X.  Work items spread evenly over the CUs; a CU running c
 // workgroups keeps c * (STAGES - 1) stages of both operand tiles in flight, each taking ~1.5 us
 // to arrive; the whole grid is further bound by HBM (~5 TB/s for the weights, read once) and by
