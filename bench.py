@@ -384,11 +384,12 @@ def main():
     # spin length: the counter rate of the spin kernel, measured
     cal0, cal1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     with torch.cuda.stream(stream):
-        cal0.record()
         torch.cuda._sleep(1_000_000)
+        cal0.record()
+        torch.cuda._sleep(10_000_000)
         cal1.record()
     torch.cuda.synchronize()
-    cycles_per_ms = 1_000_000 / max(cal0.elapsed_time(cal1), 1e-3)
+    cycles_per_ms = 10_000_000 / max(cal0.elapsed_time(cal1), 1e-3)
     spin_cycles = int(args.spin_ms * cycles_per_ms)
     with torch.cuda.stream(stream):
         for _ in range(args.steps):
