@@ -63,26 +63,13 @@ def parse():
 
 
 # ---------------------------------------------------------------------------
-# GPU-side seeded input generation (same recipe as fp8_block_scaled_gemm_amd.inputs, drawn on the
-# device so that multi-GB workloads are ready in seconds)
+# GPU-side seeded input generation (fp8_block_scaled_gemm_amd.inputs.DeviceGen: the same recipes,
+# drawn on the device so that multi-GB workloads are ready in seconds)
 # ---------------------------------------------------------------------------
 
-class Gen:
-    def __init__(self, torch, dev, seed):
-        self.t = torch
-        self.dev = dev
-        self.g = torch.Generator(device=dev)
-        self.g.manual_seed(seed)
-
-    def normal(self, shape, std=1.0):
-        return self.t.randn(shape, generator=self.g, device=self.dev, dtype=self.t.float32) * std
-
-    def activations(self, m, k):
-        a = self.normal((m, k))
-        n_out = max(1, int(round(0.01 * m)))
-        rows = self.t.randperm(m, generator=self.g, device=self.dev)[:n_out]
-        a[rows] *= 100.0
-        return a
+def Gen(torch, dev, seed):
+    from fp8_block_scaled_gemm_amd.inputs import DeviceGen
+    return DeviceGen(torch, dev, seed)
 
 
 # ---------------------------------------------------------------------------

@@ -491,18 +491,19 @@ struct Plan {
   size_t ws_bytes;   // needed workspace for this plan (0 when splits == 1)
 };
 
-static void finish_plan(Plan& pl, int64_t m, int64_t n, int64_t groups) {
+static void finish_plan(Plan& pl, int64_t m, int64_t n, int64_t k, int64_t groups) {
   const LaunchInfo li = cfg_info<kDense>(pl.cfg);
   pl.bn = li.bn;
   pl.bm = li.bm;
   pl.tiles_m = (int)((m + li.bm - 1) / li.bm);
   pl.tiles_n = (int)((n + li.bn - 1) / li.bn);
   pl.tiles = (int64_t)pl.tiles_m * pl.tiles_n * groups;
-  pl.ws_bytes = 0;
-  if (pl.splits > 1) {
-    const size_t counters = ((size_t)pl.tiles * 4 + 255) & ~(size_t)255;
-    pl.ws_bytes = counters + (size_t)pl.tiles * pl.splits * (size_t)li.bn * li.bm * 4;
+  if (pl.tiles > kMaxCounterTiles) {   // one arrival counter per tile must fit the counter prefix
+    pl.splits = 1;
+    pl.kb_per_split = (int)(k / kGroup);
   }
+  pl.ws_bytes = 0;
+  if (pl.splits > 1) pl.ws_bytes = kCounterBytes + (size_t)pl.tiles * pl.splits * (size_t)li.bn * li.bm * 4;
 }
 
 // Large-m tile choice: estimated time = rounds of the persistent grid x time per tile round.  A
@@ -565,7 +566,7 @@ static Plan make_decode_plan(int64_t m, int64_t n, int64_t k, int64_t groups, in
       pl.kb_per_split = kbps;
     }
   }
-  finish_plan(pl, m, n, groups);
+  finish_plan(pl, m, n, k, groups);
   return pl;
 }
 
@@ -588,7 +589,7 @@ static Plan make_plan(int layout, int64_t m, int64_t n, int64_t k, int64_t group
   }
   pl.kb_per_split = (kb_total + pl.splits - 1) / pl.splits;
   pl.splits = (kb_total + pl.kb_per_split - 1) / pl.kb_per_split;   // no empty split
-  finish_plan(pl, m, n, groups);
+  finish_plan(pl, m, n, k, groups);
   return pl;
 }
 
@@ -647,9 +648,8 @@ int launch_gemm(int layout, const uint8_t* a, const float* sa, int64_t ld_sa, co
   p.sb_gstride = (int64_t)p.nb128 * p.kb_total;
   p.d_gstride = m * n;
   if (pl.splits > 1) {
-    const size_t counters = ((size_t)pl.tiles * 4 + 255) & ~(size_t)255;
     p.counters = static_cast<unsigned*>(ws);
-    p.ws = reinterpret_cast<float*>(static_cast<uint8_t*>(ws) + counters);
+    p.ws = reinterpret_cast<float*>(static_cast<uint8_t*>(ws) + kCounterBytes);
   }
   switch (layout) {
     case kContiguous: return launch_layout<kContiguous>(p, pl, stream, num_cus);

@@ -97,5 +97,10 @@ __device__ __forceinline__ int masked_group_of(const int* s_prefix, int groups, 
 }
 
 constexpr int kMaxSplits = 16;   // K splits of one output tile at most
+// Split-K workspace: a fixed 64 KiB prefix of per-tile arrival counters (so that the partials of
+// one call never land where another call's counters are), then the fp32 partials.  Shapes with
+// more output tiles than counters do not split (they have plenty of tiles anyway).
+constexpr size_t kCounterBytes = 64 * 1024;
+constexpr int64_t kMaxCounterTiles = kCounterBytes / 4;
 
 }  // namespace dg

@@ -3,7 +3,8 @@
 This module only draws random numbers and builds index structures; it holds
 none of the method's arithmetic (no quantization, no GEMM).  It is the one
 module that both the HIP path's tests/bench and the CPU oracle's checks feed
-from.  Only numpy is imported.
+from.  Only numpy is imported at module level; ``DeviceGen`` draws the same
+distributions with torch's seeded generator on a device, for inputs of many GB.
 
 Workloads (the pages measure "every shape DeepSeek-V3/R1 inference may use,
 prefill and decode, without tensor parallelism" - 机器之心 DeepGEMM report,
@@ -118,3 +119,25 @@ def grouped_weights(rng, groups, n, k, std=0.02):
 def dense_v3_shapes():
     """The 18 (M, N, K) shapes of the V3-shaped dense workload, decode shapes first."""
     return [(m, n, k) for m in DENSE_V3_M for (n, k) in DENSE_V3_NK]
+
+
+class DeviceGen:
+    """The same recipes drawn on a torch device with a seeded torch generator (for workloads whose
+    fp32 inputs are GBs: the full-size tests copy only the rows the oracle checks to the host)."""
+
+    def __init__(self, torch, dev, seed):
+        self.t = torch
+        self.dev = dev
+        self.g = torch.Generator(device=dev)
+        self.g.manual_seed(int(seed))
+
+    def normal(self, shape, std=1.0):
+        return self.t.randn(shape, generator=self.g, device=self.dev, dtype=self.t.float32) * std
+
+    def activations(self, m, k, frac=0.01, factor=100.0):
+        """N(0,1) with max(1, round(frac*m)) rows, drawn without replacement, multiplied by factor."""
+        a = self.normal((m, k))
+        n_out = max(1, int(round(frac * m)))
+        rows = self.t.randperm(m, generator=self.g, device=self.dev)[:n_out]
+        a[rows] *= factor
+        return a

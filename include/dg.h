@@ -108,11 +108,12 @@ int dg_quantize_per_block(const float* w, int64_t num_groups, int64_t n, int64_t
  * a  : E4M3 (m, k) row-major.        sa : fp32, MN-major with stride ld_sa (see above).
  * b  : E4M3 (n, k) row-major.        sb : fp32 (ceil(n/128), k/128).
  * d  : bf16 (m, n) row-major, written.
- * workspace : optional device scratch for split-K on small-m shapes; it must be
- *   zero-filled before its first use and is left zero-filled in its counter
- *   area after each call; calls sharing one workspace must be ordered on one
- *   stream.  NULL or too small (see dg_gemm_workspace_size) => no split-K:
- *   still correct, slower for small m.
+ * workspace : optional device scratch for split-K on small-m shapes.  Its first
+ *   64 KiB hold per-tile arrival counters: they must be zero before the first
+ *   use (e.g. a zero-filled allocation), and every call leaves them zero; the
+ *   rest holds fp32 partials.  Calls sharing one workspace must be ordered on
+ *   one stream (concurrent calls race).  NULL or too small (see
+ *   dg_gemm_workspace_size) => no split-K: still correct, slower for small m.
  * Errors: DG_ERR_INVALID_ARG for null/misaligned pointers, negative sizes,
  * k % 128 != 0, ld_sa < m or ld_sa % 4 != 0.  Deterministic: the same inputs
  * give bit-identical outputs.

@@ -70,6 +70,22 @@ def test_split_k_deterministic():
     check_gemm(run_dense(qa, sa, qb, sb, workspace=False), ref, "no split")
 
 
+def test_split_k_shared_workspace_sequence():
+    """Split-K calls with different tile counts and splits, one after another on one workspace:
+    each call's partials must never disturb the next call's arrival counters (regression: a
+    workspace reused by a GEMM with more output tiles than the previous one)."""
+    ws = torch.zeros(64 << 20, dtype=torch.uint8, device=device())
+    shapes = [(64, 512, 4096), (64, 2112, 4096), (64, 4608, 8192), (128, 640, 4096), (64, 512, 4096)]
+    for (m, n, k) in shapes:
+        say("gemm split-k sequence", m, n, k, dg.dg_gemm_config_name(0, m, n, k))
+        assert 0 < dg.dg_gemm_workspace_size(m, n, k) <= ws.numel()
+        qa, sa, qb, sb = quantized_operands("splitseq", m, n, k)
+        d = dg.dg_gemm_fp8_nt(to_dev(qa), sa_to_dev(sa), to_dev(qb), to_dev(sb), workspace=ws)
+        torch.cuda.synchronize()
+        check_gemm(d, oracle.gemm.gemm_nt(qa, sa, qb, sb), f"split sequence {m}x{n}x{k}")
+    assert int(ws[:64 << 10].count_nonzero()) == 0, "arrival counters not left at zero"
+
+
 def test_closed_form_all_448():
     say("gemm all-448")
     a = np.full((96, 512), 448.0, np.float32)
