@@ -246,18 +246,22 @@ __global__ __launch_bounds__(C::kThreads) void gemm_fp8_kernel(GemmParams p) {
       for (int j = 0; j < C::kFragM; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
 
     // Issue the stage group of local K block tk (absolute kb_begin + tk) into ring slot SLOT:
-    // kDmaPerWave operand DMAs and one scale DMA per thread (the vmcnt accounting counts
-    // kVmPerStage per group); the weight scale is a scalar load.
+    // kDmaPerWave operand DMAs and the activation- and weight-scale DMAs (the vmcnt accounting
+    // counts kVmPerStage per group).
     auto issue = [&](int tk, auto slot_c) {
       constexpr int slot = decltype(slot_c)::value;
       const int kb = kb_begin + tk;
       uint8_t* sbase = slot == 0 ? st0 : slot == 1 ? st1 : slot == 2 ? st2 : st3;
+      // the per-band offsets are recomputed at every issue (one add each) from an opaque copy
+      // of the band-0 offset, rather than kept live in a register per band across the main loop
+      uint32_t base_off = dma_off;
+      asm volatile("" : "+v"(base_off));
 #pragma unroll
       for (int u = 0; u < C::kDmaPerWave; ++u) {
         const int q = wave + C::kWaves * u;
         const bool is_b = u < kBandsB;
         lds_dma16(is_b ? rs_b : rs_a, sbase + q * (C::kDmaRows * kGroup),
-                  dma_off + (uint32_t)(is_b ? u : u - kBandsB) * band_step, kb * kGroup);
+                  base_off + (uint32_t)(is_b ? u : u - kBandsB) * band_step, kb * kGroup);
       }
       if (sa_active)
         lds_dma16(rs_sa, sbase + C::kSaOffset + 16 * wave * C::kSaLanesPerWave, sa_src, kb * (int)p.ld_sa * 4);
@@ -309,6 +313,9 @@ __global__ __launch_bounds__(C::kThreads) void gemm_fp8_kernel(GemmParams p) {
       for (int q = 0; q <= Q; ++q) {
         if (q < Q) {
           const int i = q / C::kFragM, j = q % C::kFragM;
+          // fragment row i: nothing of a later row may be scheduled above this point, so at most
+          // two weight fragments are live (the one in use and the one being read)
+          if (j == 0) __builtin_amdgcn_sched_barrier(0);
           if (j == 0 && i + 1 < C::kFragN) aop[(i + 1) & 1] = read_a(i + 1);
           part[q & 1] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
               aop[i & 1], bop[j], v4f{0.f, 0.f, 0.f, 0.f}, 0, 0, 0, 127, 0, 127);

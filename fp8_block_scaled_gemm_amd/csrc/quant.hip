@@ -14,48 +14,45 @@
 namespace dg {
 
 // ---------------------------------------------------------------------------
-// 1 x 128 groups along K (activations), for `groups` stacked (m, k) matrices.
-// A half-wave (32 lanes x 4 floats) owns one 128-wide group; consecutive
-// half-waves take consecutive rows of the same K group so that the MN-major
-// scale stores are contiguous.  Group index gi = (g * KB + kb) * m + row.
+// 1 x 128 groups along K (activations), for `mats` stacked (m, k) matrices.
+// A half-wave (32 lanes x 4 floats) owns one 128-wide group.  A 256-thread workgroup takes 8
+// consecutive rows (of the stacked rows) x kTokKb consecutive K groups: grid (row blocks,
+// K-group blocks), so each half-wave splits its row index once (32-bit) and the loads of its
+// kTokKb groups are all in flight together.  The 8 half-waves of one K group store 8
+// consecutive scales.
 // ---------------------------------------------------------------------------
 constexpr int kTokThreads = 256;
-constexpr int kTokUnroll = 4;   // groups per lane per iteration (loads in flight)
+constexpr int kTokRows = kTokThreads / 32;   // rows per workgroup
+constexpr int kTokKb = 4;                    // K groups per workgroup (loads in flight per lane)
 
 __global__ __launch_bounds__(kTokThreads) void quant_token_group_kernel(
-    const float* __restrict__ x, int64_t m, int64_t k, uint8_t* __restrict__ q,
-    float* __restrict__ sa, int64_t ld_sa, int64_t groups) {
+    const float* __restrict__ x, int m, int k, uint8_t* __restrict__ q,
+    float* __restrict__ sa, int64_t ld_sa, int total_rows) {
   const int lane = threadIdx.x & 31;
-  const int64_t half_waves = ((int64_t)gridDim.x * kTokThreads) >> 5;
-  const int64_t first = ((int64_t)blockIdx.x * kTokThreads + threadIdx.x) >> 5;
+  const int row = blockIdx.x * kTokRows + (threadIdx.x >> 5);   // stacked row: g * m + r
+  if (row >= total_rows) return;                                 // uniform per half-wave
+  const int kbc = k / kGroup;
+  const int kb0 = blockIdx.y * kTokKb;
+  const int g = row / m, r = row - g * m;
+  const float* src = x + (int64_t)row * k + kb0 * kGroup;
+  uint8_t* dst = q + (int64_t)row * k + kb0 * kGroup;
+  float* scl = sa + ((int64_t)g * kbc + kb0) * ld_sa + r;
 
-  for (int64_t base = first; base < groups; base += half_waves * kTokUnroll) {
-    v4f v[kTokUnroll];
+  v4f v[kTokKb];
 #pragma unroll
-    for (int u = 0; u < kTokUnroll; ++u) {
-      const int64_t gi = base + u * half_waves;
-      if (gi < groups) {
-        const int64_t gkb = gi / m, row = gi - gkb * m;      // gkb = g * KB + kb
-        const int64_t kbc = k / kGroup, g = gkb / kbc, kb = gkb - g * kbc;
-        v[u] = __builtin_nontemporal_load(
-            reinterpret_cast<const v4f*>(x + (g * m + row) * k + kb * kGroup) + lane);
-      }
-    }
+  for (int u = 0; u < kTokKb; ++u)
+    if (kb0 + u < kbc) v[u] = __builtin_nontemporal_load(reinterpret_cast<const v4f*>(src + u * kGroup) + lane);
 #pragma unroll
-    for (int u = 0; u < kTokUnroll; ++u) {
-      const int64_t gi = base + u * half_waves;
-      if (gi >= groups) break;   // uniform across the half-wave
-      const int64_t gkb = gi / m, row = gi - gkb * m;
-      const int64_t kbc = k / kGroup, g = gkb / kbc, kb = gkb - g * kbc;
-      float amax = fmaxf(fmaxf(fabsf(v[u].x), fabsf(v[u].y)), fmaxf(fabsf(v[u].z), fabsf(v[u].w)));
+  for (int u = 0; u < kTokKb; ++u) {
+    if (kb0 + u >= kbc) break;   // uniform
+    float amax = fmaxf(fmaxf(fabsf(v[u].x), fabsf(v[u].y)), fmaxf(fabsf(v[u].z), fabsf(v[u].w)));
 #pragma unroll
-      for (int off = 16; off > 0; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off, 32));
-      const float s = amax == 0.0f ? 1.0f : amax / kE4M3Max;
-      const uint32_t packed = pack4_e4m3(clamp448(v[u].x / s), clamp448(v[u].y / s),
-                                         clamp448(v[u].z / s), clamp448(v[u].w / s));
-      reinterpret_cast<uint32_t*>(q + (g * m + row) * k + kb * kGroup)[lane] = packed;
-      if (lane == 0) sa[gkb * ld_sa + row] = s;
-    }
+    for (int off = 16; off > 0; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off, 32));
+    const float s = amax == 0.0f ? 1.0f : amax / kE4M3Max;
+    const uint32_t packed = pack4_e4m3(clamp448(v[u].x / s), clamp448(v[u].y / s),
+                                       clamp448(v[u].z / s), clamp448(v[u].w / s));
+    reinterpret_cast<uint32_t*>(dst + u * kGroup)[lane] = packed;
+    if (lane == 0) scl[(int64_t)u * ld_sa] = s;
   }
 }
 
@@ -119,14 +116,17 @@ __global__ __launch_bounds__(kBlkThreads) void quant_block_kernel(
 // ---------------------------------------------------------------------------
 int launch_quant_token_group(const float* x, int64_t mats, int64_t m, int64_t k, uint8_t* q, float* sa,
                              int64_t ld_sa, hipStream_t stream, int num_cus) {
-  const int64_t groups = mats * m * (k / kGroup);
-  const int64_t groups_per_block = kTokThreads / 32;
-  int64_t blocks = (groups + groups_per_block * kTokUnroll - 1) / (groups_per_block * kTokUnroll);
-  const int64_t cap = (int64_t)num_cus * 16;   // enough resident waves to cover HBM latency
-  if (blocks > cap) blocks = cap;
-  if (blocks < 1) blocks = 1;
-  hipLaunchKernelGGL(quant_token_group_kernel, dim3((unsigned)blocks), dim3(kTokThreads), 0,
-                     stream, x, m, k, q, sa, ld_sa, groups);
+  (void)num_cus;
+  const int64_t total_rows = mats * m;
+  const int64_t kbc = k / kGroup;
+  if (total_rows > 0x7fffffffLL || k > 0x7fffffffLL)
+    return set_error(kUnsupported, "quantize_per_token_group: more than 2^31 rows or columns");
+  const int64_t gx = (total_rows + kTokRows - 1) / kTokRows;
+  const int64_t gy = (kbc + kTokKb - 1) / kTokKb;
+  if (gx > 0x7fffffffLL || gy > 65535)
+    return set_error(kUnsupported, "quantize_per_token_group: shape too large for the launch grid");
+  hipLaunchKernelGGL(quant_token_group_kernel, dim3((unsigned)gx, (unsigned)gy), dim3(kTokThreads), 0, stream,
+                     x, (int)m, (int)k, q, sa, ld_sa, (int)total_rows);
   const hipError_t e = hipGetLastError();
   return e == hipSuccess ? kOk : set_error(kHip, "quantize_per_token_group launch: %s", hipGetErrorString(e));
 }
