@@ -514,16 +514,16 @@ static void finish_plan(Plan& pl, int64_t m, int64_t n, int64_t k, int64_t group
 }
 
 // Large-m tile choice: estimated time = rounds of the persistent grid x time per tile round.  A
-// 256x192 tile round takes ~1.36x a 256x128 round (1.5x the MFMA work, less operand traffic per
-// flop: measured on 16384x7168x16384), so it wins where it saves a round, e.g. 4096x2112 (198
-// tiles, one round, vs 288) or 4096x32768 (11 rounds vs 16).
+// 256x192 tile round takes ~1.22x a 256x128 round (1.5x the MFMA work, less operand traffic per
+// flop; measured on MI355X over nine shapes with M = 2048..16384), so it wins where it saves a
+// round, e.g. 4096x2112 (198 tiles, one round, vs 288) or 4096x7168 (3 rounds vs 3.5).
 static int choose_large(int64_t m, int64_t n, int64_t groups, int num_cus) {
   auto rounds = [&](int bn, int bm) {
     const int64_t tiles = ((m + bm - 1) / bm) * ((n + bn - 1) / bn) * groups;
     return (tiles + num_cus - 1) / num_cus;   // both configurations run one workgroup per CU
   };
   const double t_large = (double)rounds(CfgLarge::BN, CfgLarge::BM);
-  const double t_wide = 1.36 * (double)rounds(CfgWide::BN, CfgWide::BM);
+  const double t_wide = 1.22 * (double)rounds(CfgWide::BN, CfgWide::BM);
   return t_wide < t_large ? kCfgWide : kCfgLarge;
 }
 
