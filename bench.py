@@ -55,6 +55,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target CPU work of the oracle sample")
     ap.add_argument("--eager", action="store_true", help="time eager launches instead of graph replays")
+    ap.add_argument("--act-dtype", default="fp32", choices=["fp32", "bf16"],
+                    help="activation input type of the dense workloads (bf16: the bf16-input quantizer)")
     ap.add_argument("--spin-ms", type=float, default=20.0,
                     help="device spin before each per-kernel timing pass (covers the host's enqueue time)")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -88,13 +90,14 @@ def dense_gemm_bytes(m, n, k):
     return m * k + 4 * m * (k // 128) + n * k + 4 * (-(-n // 128)) * (k // 128) + 2 * m * n
 
 
-def quant_bytes(elems, k):
-    """fp32 read + E4M3 write + one fp32 scale per 128 elements."""
-    return 4 * elems + elems + 4 * elems // 128
+def quant_bytes(elems, k, in_bytes=4):
+    """input read (fp32 or bf16) + E4M3 write + one fp32 scale per 128 elements."""
+    return in_bytes * elems + elems + 4 * elems // 128
 
 
-def build_dense(torch, dg, dev, shapes, name):
-    """Ops for a list of dense (M, N, K) shapes sharing weights per (N, K)."""
+def build_dense(torch, dg, dev, shapes, name, act_dtype="fp32"):
+    """Ops for a list of dense (M, N, K) shapes sharing weights per (N, K).  act_dtype "bf16": the
+    activations arrive in bf16 and go through the bf16-input quantizer."""
     gen = Gen(torch, dev, 1234)
     ops = []
     weights = {}
@@ -110,13 +113,15 @@ def build_dense(torch, dg, dev, shapes, name):
     for (m, n, k) in shapes:
         w32, qb, sb = weights[(n, k)]
         a32 = gen.activations(m, k)
+        if act_dtype == "bf16":
+            a32 = a32.to(torch.bfloat16)
         qa = torch.empty((m, k), dtype=torch.uint8, device=dev)
         sa = torch.empty((k // 128, dg.dg_get_scale_ld(m)), dtype=torch.float32, device=dev)
         d = torch.empty((m, n), dtype=torch.bfloat16, device=dev)
         ws = dg.default_workspace(dev, dg.dg_gemm_workspace_size(m, n, k, 1))
         ops.append(Op("aquant", f"aq {m}x{k}",
                       (lambda a32=a32, qa=qa, sa=sa: dg.dg_quantize_per_token_group(a32, q=qa, sa=sa)),
-                      nbytes=quant_bytes(m * k, k)))
+                      nbytes=quant_bytes(m * k, k, 2 if act_dtype == "bf16" else 4)))
         ops.append(Op("gemm", f"{m}x{n}x{k}",
                       (lambda qa=qa, sa=sa, qb=qb, sb=sb, d=d, ws=ws: dg.dg_gemm_fp8_nt(qa, sa, qb, sb, d=d,
                                                                                          workspace=ws)),
@@ -191,8 +196,10 @@ def build_masked(torch, dg, dev, cases):
     return ops
 
 
-def build_workload(name, torch, dg, dev):
+def build_workload(name, torch, dg, dev, act_dtype="fp32"):
     from fp8_block_scaled_gemm_amd import inputs
+    if act_dtype != "fp32" and name not in ("dense_v3", "small", "large_dense"):
+        raise SystemExit(f"bench.py: --act-dtype {act_dtype} applies to the dense workloads only")
     if name == "dense_v3":
         # decode shapes first, then prefill, then the second decode size: the weights read by the two
         # decode passes are separated by > 1 GB of traffic, so neither pass is served by the 256 MB MALL
@@ -200,11 +207,12 @@ def build_workload(name, torch, dg, dev):
         shapes = [(m, n, k) for m in order for (n, k) in inputs.DENSE_V3_NK]
         desc = ("DeepSeek-V3 dense GEMMs: M in {64,128,4096} x (N,K) in {(2112,7168),(24576,1536),"
                 "(32768,512),(7168,16384),(4096,7168),(7168,2048)}; A~N(0,1) with 1% rows x100, B~N(0,0.02^2)")
-        return build_dense(torch, dg, dev, shapes, name), desc
+        return build_dense(torch, dg, dev, shapes, name, act_dtype), desc
     if name == "small":
-        return build_dense(torch, dg, dev, [(128, 512, 512)], name), "M=128, N=512, K=512"
+        return build_dense(torch, dg, dev, [(128, 512, 512)], name, act_dtype), "M=128, N=512, K=512"
     if name == "large_dense":
-        return build_dense(torch, dg, dev, [(16384, 7168, 16384)], name), "dense prefill M=16384, N=7168, K=16384"
+        return (build_dense(torch, dg, dev, [(16384, 7168, 16384)], name, act_dtype),
+                "dense prefill M=16384, N=7168, K=16384")
     if name == "contiguous":
         cases = []
         for g in (4, 8):
@@ -323,7 +331,7 @@ def main():
         copy_calibration(torch, dev)
         return
     dg.lib()
-    ops, desc = build_workload(args.workload, torch, dg, dev)
+    ops, desc = build_workload(args.workload, torch, dg, dev, args.act_dtype)
     torch.cuda.synchronize()
     print(f"[bench] workload {args.workload}: {len(ops)} ops per step", file=sys.stderr, flush=True)
 
@@ -454,6 +462,7 @@ def main():
            "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4), "higher_is_better": True,
            "scaling": "weak", "vs_baseline": None, "dtype": "fp8_e4m3", "data": "synthetic",
            "config": {"workload": args.workload, "description": desc, "gemms": len(shapes),
+                      "activation_input": args.act_dtype,
                       "step": "weight quantization (all weights) + per shape: activation quantization, FP8 GEMM",
                       "timing": "eager" if graph is None else "hip graph replay per step",
                       "device_ms_per_step": round(gpu_ms_per_step, 4),

@@ -7,7 +7,8 @@ is not built, every call raises - there is no fallback.
 
 Functions carry the C names:
 
-* ``dg_quantize_per_token_group(x)``  -> (q uint8 (M, K), sa float32 (K/128, ld_sa))
+* ``dg_quantize_per_token_group(x)``  -> (q uint8 (M, K), sa float32 (K/128, ld_sa)); fp32 or
+  bf16 x (the bf16 entry point is ``dg_quantize_per_token_group_bf16``)
 * ``dg_quantize_per_block(w)``        -> (q uint8 like w, sb float32 ([G,] ceil(N/128), K/128))
 * ``dg_gemm_fp8_nt(a, sa, b, sb)``    -> d bf16 (M, N)
 * ``dg_gemm_fp8_grouped_contiguous(a, sa, b, sb, m_indices)``  -> d bf16 (M_total, N)
@@ -39,6 +40,8 @@ _SIGNATURES = {
     "dg_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "dg_last_error_message": (ctypes.c_char_p, []),
     "dg_quantize_per_token_group": (ctypes.c_int, [_vp, _c_int64, _c_int64, _c_int64, _vp, _vp, _c_int64, _vp]),
+    "dg_quantize_per_token_group_bf16": (ctypes.c_int, [_vp, _c_int64, _c_int64, _c_int64, _vp, _vp, _c_int64,
+                                                        _vp]),
     "dg_quantize_per_block": (ctypes.c_int, [_vp, _c_int64, _c_int64, _c_int64, _vp, _vp, _vp]),
     "dg_gemm_fp8_nt": (ctypes.c_int, [_vp, _vp, _c_int64, _vp, _vp, _vp, _c_int64, _c_int64, _c_int64,
                                       _vp, ctypes.c_size_t, _vp]),
@@ -161,9 +164,11 @@ def default_workspace(device, nbytes):
 # ---------------------------------------------------------------------------
 
 def dg_quantize_per_token_group(x, q=None, sa=None):
-    """x float32 (M, K) -> (q uint8 (M, K), sa float32 (K/128, ld_sa)); or x (G, M, K) ->
-    (q (G, M, K), sa (G, K/128, ld_sa)) for the per-expert masked layout.  Runs on x's stream."""
-    _require(x.dtype == torch.float32 and x.dim() in (2, 3), "x must be float32 (M, K) or (G, M, K)")
+    """x float32 or bfloat16 (M, K) -> (q uint8 (M, K), sa float32 (K/128, ld_sa)); or x (G, M, K)
+    -> (q (G, M, K), sa (G, K/128, ld_sa)) for the per-expert masked layout.  Runs on x's stream.
+    bfloat16 input goes to dg_quantize_per_token_group_bf16 (same result as the widened fp32)."""
+    _require(x.dtype in (torch.float32, torch.bfloat16) and x.dim() in (2, 3),
+             "x must be float32 or bfloat16, (M, K) or (G, M, K)")
     grouped = x.dim() == 3
     g, m, k = (x.shape if grouped else (1,) + tuple(x.shape))
     kb = k // 128 if k % 128 == 0 else 0
@@ -174,9 +179,15 @@ def dg_quantize_per_token_group(x, q=None, sa=None):
                          dtype=torch.float32, device=x.device)
     q = _bytes(q)
     _dev(x, q, sa)
-    _check("dg_quantize_per_token_group",
-           lib().dg_quantize_per_token_group(_ptr(x), g, m, k, _ptr(q), _ptr(sa), sa.shape[-1], _stream(x)))
+    name = "dg_quantize_per_token_group" + ("_bf16" if x.dtype == torch.bfloat16 else "")
+    _check(name, getattr(lib(), name)(_ptr(x), g, m, k, _ptr(q), _ptr(sa), sa.shape[-1], _stream(x)))
     return q, sa
+
+
+def dg_quantize_per_token_group_bf16(x, q=None, sa=None):
+    """bfloat16 x (M, K) or (G, M, K) -> (q, sa): dg_quantize_per_token_group_bf16."""
+    _require(x.dtype == torch.bfloat16, "x must be bfloat16")
+    return dg_quantize_per_token_group(x, q=q, sa=sa)
 
 
 def dg_quantize_per_block(w, q=None, sb=None):

@@ -15,7 +15,9 @@
 namespace dg {
 
 int launch_quant_token_group(const float* x, int64_t groups, int64_t m, int64_t k, uint8_t* q, float* sa,
-                             int64_t ld_sa, hipStream_t stream, int num_cus);
+                             int64_t ld_sa, hipStream_t stream);
+int launch_quant_token_group_bf16(const uint16_t* x, int64_t groups, int64_t m, int64_t k, uint8_t* q, float* sa,
+                                  int64_t ld_sa, hipStream_t stream);
 int launch_quant_block(const float* w, int64_t groups, int64_t n, int64_t k, uint8_t* q, float* sb,
                        hipStream_t stream);
 int launch_gemm(int layout, const uint8_t* a, const float* sa, int64_t ld_sa, const uint8_t* b,
@@ -109,8 +111,8 @@ size_t dg_gemm_workspace_size(int64_t m, int64_t n, int64_t k, int64_t num_group
   return gemm_workspace_size(m, n, k, num_groups, cus);
 }
 
-int dg_quantize_per_token_group(const float* x, int64_t num_groups, int64_t m, int64_t k, uint8_t* q,
-                                float* sa, int64_t ld_sa, dg_stream_t stream) {
+static int check_token_group(const void* x, int64_t num_groups, int64_t m, int64_t k, uint8_t* q, float* sa,
+                             int64_t ld_sa) {
   DG_REQUIRE(num_groups >= 0 && m >= 0 && k > 0 && k % kGroup == 0,
              "quantize_per_token_group: need groups >= 0, m >= 0, k > 0, k %% 128 == 0 (m=%lld k=%lld)",
              (long long)m, (long long)k);
@@ -119,9 +121,21 @@ int dg_quantize_per_token_group(const float* x, int64_t num_groups, int64_t m, i
   if (m == 0 || num_groups == 0) return DG_OK;
   DG_REQUIRE(x && q && sa, "quantize_per_token_group: null pointer");
   DG_REQUIRE(aligned16(x) && aligned16(q) && aligned16(sa), "quantize_per_token_group: pointers must be 16-byte aligned");
-  const int cus = effective_cus();
-  if (cus < 0) return cus;
-  return launch_quant_token_group(x, num_groups, m, k, q, sa, ld_sa, static_cast<hipStream_t>(stream), cus);
+  return 1;   // proceed
+}
+
+int dg_quantize_per_token_group(const float* x, int64_t num_groups, int64_t m, int64_t k, uint8_t* q,
+                                float* sa, int64_t ld_sa, dg_stream_t stream) {
+  const int c = check_token_group(x, num_groups, m, k, q, sa, ld_sa);
+  if (c <= 0) return c;
+  return launch_quant_token_group(x, num_groups, m, k, q, sa, ld_sa, static_cast<hipStream_t>(stream));
+}
+
+int dg_quantize_per_token_group_bf16(const uint16_t* x, int64_t num_groups, int64_t m, int64_t k, uint8_t* q,
+                                     float* sa, int64_t ld_sa, dg_stream_t stream) {
+  const int c = check_token_group(x, num_groups, m, k, q, sa, ld_sa);
+  if (c <= 0) return c;
+  return launch_quant_token_group_bf16(x, num_groups, m, k, q, sa, ld_sa, static_cast<hipStream_t>(stream));
 }
 
 int dg_quantize_per_block(const float* w, int64_t num_groups, int64_t n, int64_t k, uint8_t* q,

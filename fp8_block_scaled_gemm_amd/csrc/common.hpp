@@ -4,6 +4,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 namespace dg {
 
 typedef int v8i __attribute__((ext_vector_type(8)));
@@ -40,5 +42,39 @@ __device__ __forceinline__ uint32_t pack4_e4m3(float y0, float y1, float y2, flo
 }
 
 __device__ __forceinline__ float clamp448(float v) { return fminf(fmaxf(v, -kE4M3Max), kE4M3Max); }
+
+// max over each 16-lane row of the wave, by DPP lane swaps (VALU, no LDS crossbar): xor 1 and
+// xor 2 inside quads, then the half-row and row mirrors.  Every lane gets its row's maximum.
+__device__ __forceinline__ float row16_max(float v) {
+  auto dpp = [](float x, auto ctrl_c) {
+    constexpr int ctrl = decltype(ctrl_c)::value;
+    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), ctrl, 0xf, 0xf, false));
+  };
+  v = fmaxf(v, dpp(v, std::integral_constant<int, 0xB1>{}));    // quad_perm [1,0,3,2]
+  v = fmaxf(v, dpp(v, std::integral_constant<int, 0x4E>{}));    // quad_perm [2,3,0,1]
+  v = fmaxf(v, dpp(v, std::integral_constant<int, 0x141>{}));   // row_half_mirror
+  v = fmaxf(v, dpp(v, std::integral_constant<int, 0x140>{}));   // row_mirror
+  return v;
+}
+
+// max over each 32-lane half of the wave (lanes 0-31 and 32-63), returned to every lane of the half.
+__device__ __forceinline__ float half_wave_max(float v) {
+  v = row16_max(v);
+  const float r0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0));
+  const float r1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 16));
+  const float r2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 32));
+  const float r3 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 48));
+  return (threadIdx.x & 32) ? fmaxf(r2, r3) : fmaxf(r0, r1);
+}
+
+// max over the whole wave, returned to every lane.
+__device__ __forceinline__ float wave_max(float v) {
+  v = row16_max(v);
+  const float r0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0));
+  const float r1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 16));
+  const float r2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 32));
+  const float r3 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 48));
+  return fmaxf(fmaxf(r0, r1), fmaxf(r2, r3));
+}
 
 }  // namespace dg

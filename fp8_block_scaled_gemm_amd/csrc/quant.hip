@@ -7,8 +7,9 @@
 // Both divisions are IEEE fp32 divisions (the library is built without fast
 // math), so bytes and scales are bit-exact with any correct implementation.
 //
-// Both kernels are HBM-bound streaming kernels (read 4 B, write 1 B + 1/32 B
-// per element): 16-byte coalesced loads, several loads in flight per lane.
+// Both kernels are HBM-bound streaming kernels (read 4 B - 2 B for bf16 activations -, write
+// 1 B + 1/32 B per element): coalesced 16-byte (8-byte for bf16) loads, several in flight per
+// lane.  Group maxima use DPP lane swaps and lane reads (no LDS crossbar).
 #include "common.hpp"
 
 namespace dg {
@@ -25,8 +26,21 @@ constexpr int kTokThreads = 256;
 constexpr int kTokRows = kTokThreads / 32;   // rows per workgroup
 constexpr int kTokKb = 4;                    // K groups per workgroup (loads in flight per lane)
 
+// Four consecutive activations of a lane as fp32: fp32 input as is, bf16 input widened exactly
+// (a bf16 value is the upper half of the fp32 word).
+__device__ __forceinline__ v4f load4(const float* p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const v4f*>(p));
+}
+__device__ __forceinline__ v4f load4(const uint16_t* p) {
+  typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+  const u32x2 w = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(p));
+  return v4f{__uint_as_float(w.x << 16), __uint_as_float(w.x & 0xffff0000u), __uint_as_float(w.y << 16),
+             __uint_as_float(w.y & 0xffff0000u)};
+}
+
+template <class T>
 __global__ __launch_bounds__(kTokThreads) void quant_token_group_kernel(
-    const float* __restrict__ x, int m, int k, uint8_t* __restrict__ q,
+    const T* __restrict__ x, int m, int k, uint8_t* __restrict__ q,
     float* __restrict__ sa, int64_t ld_sa, int total_rows) {
   const int lane = threadIdx.x & 31;
   const int row = blockIdx.x * kTokRows + (threadIdx.x >> 5);   // stacked row: g * m + r
@@ -34,20 +48,19 @@ __global__ __launch_bounds__(kTokThreads) void quant_token_group_kernel(
   const int kbc = k / kGroup;
   const int kb0 = blockIdx.y * kTokKb;
   const int g = row / m, r = row - g * m;
-  const float* src = x + (int64_t)row * k + kb0 * kGroup;
+  const T* src = x + (int64_t)row * k + kb0 * kGroup;
   uint8_t* dst = q + (int64_t)row * k + kb0 * kGroup;
   float* scl = sa + ((int64_t)g * kbc + kb0) * ld_sa + r;
 
   v4f v[kTokKb];
 #pragma unroll
   for (int u = 0; u < kTokKb; ++u)
-    if (kb0 + u < kbc) v[u] = __builtin_nontemporal_load(reinterpret_cast<const v4f*>(src + u * kGroup) + lane);
+    if (kb0 + u < kbc) v[u] = load4(src + u * kGroup + 4 * lane);
 #pragma unroll
   for (int u = 0; u < kTokKb; ++u) {
     if (kb0 + u >= kbc) break;   // uniform
-    float amax = fmaxf(fmaxf(fabsf(v[u].x), fabsf(v[u].y)), fmaxf(fabsf(v[u].z), fabsf(v[u].w)));
-#pragma unroll
-    for (int off = 16; off > 0; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off, 32));
+    const float amax =
+        half_wave_max(fmaxf(fmaxf(fabsf(v[u].x), fabsf(v[u].y)), fmaxf(fabsf(v[u].z), fabsf(v[u].w))));
     const float s = amax == 0.0f ? 1.0f : amax / kE4M3Max;
     const uint32_t packed = pack4_e4m3(clamp448(v[u].x / s), clamp448(v[u].y / s),
                                        clamp448(v[u].z / s), clamp448(v[u].w / s));
@@ -91,8 +104,7 @@ __global__ __launch_bounds__(kBlkThreads) void quant_block_kernel(
       amax = fmaxf(amax, fmaxf(fmaxf(fabsf(v[u].x), fabsf(v[u].y)), fmaxf(fabsf(v[u].z), fabsf(v[u].w))));
     }
   }
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off, 64));
+  amax = wave_max(amax);
   __shared__ float red[kBlkThreads / 64];
   if ((tid & 63) == 0) red[tid >> 6] = amax;
   __syncthreads();
@@ -114,9 +126,9 @@ __global__ __launch_bounds__(kBlkThreads) void quant_block_kernel(
 // ---------------------------------------------------------------------------
 // Launchers (arguments already validated by the C ABI layer).
 // ---------------------------------------------------------------------------
-int launch_quant_token_group(const float* x, int64_t mats, int64_t m, int64_t k, uint8_t* q, float* sa,
-                             int64_t ld_sa, hipStream_t stream, int num_cus) {
-  (void)num_cus;
+template <class T>
+static int launch_token_group(const T* x, int64_t mats, int64_t m, int64_t k, uint8_t* q, float* sa,
+                              int64_t ld_sa, hipStream_t stream) {
   const int64_t total_rows = mats * m;
   const int64_t kbc = k / kGroup;
   if (total_rows > 0x7fffffffLL || k > 0x7fffffffLL)
@@ -125,10 +137,20 @@ int launch_quant_token_group(const float* x, int64_t mats, int64_t m, int64_t k,
   const int64_t gy = (kbc + kTokKb - 1) / kTokKb;
   if (gx > 0x7fffffffLL || gy > 65535)
     return set_error(kUnsupported, "quantize_per_token_group: shape too large for the launch grid");
-  hipLaunchKernelGGL(quant_token_group_kernel, dim3((unsigned)gx, (unsigned)gy), dim3(kTokThreads), 0, stream,
+  hipLaunchKernelGGL(quant_token_group_kernel<T>, dim3((unsigned)gx, (unsigned)gy), dim3(kTokThreads), 0, stream,
                      x, (int)m, (int)k, q, sa, ld_sa, (int)total_rows);
   const hipError_t e = hipGetLastError();
   return e == hipSuccess ? kOk : set_error(kHip, "quantize_per_token_group launch: %s", hipGetErrorString(e));
+}
+
+int launch_quant_token_group(const float* x, int64_t mats, int64_t m, int64_t k, uint8_t* q, float* sa,
+                             int64_t ld_sa, hipStream_t stream) {
+  return launch_token_group(x, mats, m, k, q, sa, ld_sa, stream);
+}
+
+int launch_quant_token_group_bf16(const uint16_t* x, int64_t mats, int64_t m, int64_t k, uint8_t* q, float* sa,
+                                  int64_t ld_sa, hipStream_t stream) {
+  return launch_token_group(x, mats, m, k, q, sa, ld_sa, stream);
 }
 
 int launch_quant_block(const float* w, int64_t groups, int64_t n, int64_t k, uint8_t* q, float* sb,

@@ -55,6 +55,14 @@ def activations_with_outliers(rng, m, k, frac=0.01, factor=100.0):
     return a
 
 
+def to_bf16_bits(x):
+    """float32 -> bf16 bit patterns (uint16), round to nearest even: how a bf16 activation
+    tensor of these values would hold them (input data for the bf16-input quantizer)."""
+    u = np.asarray(x, dtype=np.float32).view(np.uint32).astype(np.uint64)
+    r = (u + np.uint64(0x7FFF) + ((u >> np.uint64(16)) & np.uint64(1))) >> np.uint64(16)
+    return r.astype(np.uint16)
+
+
 def pad_to(x, align=ALIGN_M):
     return -(-int(x) // align) * align
 

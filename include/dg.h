@@ -88,6 +88,17 @@ int dg_quantize_per_token_group(const float* x, int64_t num_groups, int64_t m, i
                                 float* sa, int64_t ld_sa, dg_stream_t stream);
 
 /*
+ * The same per-token-group quantizer for bf16 activations (x : bf16 bits, (num_groups,
+ * m, k) row-major).  A bf16 value widens to fp32 exactly, so the bytes and scales are those
+ * dg_quantize_per_token_group gives for the widened values.  Activations of this path are
+ * commonly bf16 (the GEMM's own output format: 机器之心 report, "quick start"); reading them
+ * directly halves the quantizer's input traffic (2 B instead of 4 B per element).
+ * Same layouts, errors and guarantees as dg_quantize_per_token_group.
+ */
+int dg_quantize_per_token_group_bf16(const uint16_t* x, int64_t num_groups, int64_t m, int64_t k, uint8_t* q,
+                                     float* sa, int64_t ld_sa, dg_stream_t stream);
+
+/*
  * Per-block weight quantizer (128 x 128), for num_groups stacked (n, k) matrices.
  * Same rule as above with the amax over each 128 x 128 block (a partial last
  * block at the N edge takes its amax over the rows present).

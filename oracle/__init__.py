@@ -16,6 +16,7 @@ news/blog pages; each function cites the page title and section it follows):
   opening section; CSDN "DeepGEMM: concise, efficient ..." article, "what is
   DeepGEMM"): one fp32 scale per 1x128 activation group and per 128x128 weight
   block, scale = amax / 448.
+* ``bf16``  - exact widening of bf16 activations to fp32 (for the bf16-input quantizer).
 * ``gemm``  - the three GEMM forms the pages list (normal, contiguous-grouped,
   masked-grouped: 机器之心 report, "quick start"; ai.abqq.net summary, section 3;
   3loumao explainer, section 03): dequantise exactly and multiply in fp64.
@@ -25,4 +26,4 @@ do not come from this package (the format definition, torch's independent
 float8_e4m3fn codec, exact rational arithmetic, closed forms, invariants).
 """
 
-from . import e4m3, quant, gemm  # noqa: F401
+from . import bf16, e4m3, quant, gemm  # noqa: F401

@@ -19,7 +19,7 @@ division is correctly rounded), exactly as the GPU path must do it.
 
 import numpy as np
 
-from . import e4m3
+from . import bf16, e4m3
 
 GROUP = 128
 _F448 = np.float32(448.0)
@@ -48,6 +48,12 @@ def quantize_per_token_group(x):
     y = (g / s[:, :, None]).astype(np.float32)           # IEEE fp32 division
     q = e4m3.encode(y).reshape(m, k)
     return q, s
+
+
+def quantize_per_token_group_bf16(bits):
+    """The per-token-group quantizer on bf16 activations (bits as uint16, (M, K)): the values
+    are widened to fp32 exactly (oracle.bf16.decode) and quantized as above."""
+    return quantize_per_token_group(bf16.decode(bits))
 
 
 def quantize_per_block(w):

@@ -434,6 +434,41 @@ def pin_gemm_grouped(seed=29):
         np.testing.assert_array_equal(dfull[e], oracle.gemm.gemm_nt(qam[e], sam[e], qb[e], sb[e]))
 
 
+def pin_bf16_decode_vs_torch():
+    """All 65536 bf16 patterns widen to the same fp32 bits as torch's bfloat16 -> float32 cast."""
+    bits = np.arange(1 << 16, dtype=np.uint32).astype(np.uint16)
+    ref = torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).to(torch.float32).numpy()
+    got = oracle.bf16.decode(bits)
+    finite = np.isfinite(ref)
+    assert np.array_equal(ref[finite].view(np.uint32), got[finite].view(np.uint32))
+    assert np.array_equal(np.isnan(ref), np.isnan(got)) and np.array_equal(np.isinf(ref), np.isinf(got))
+
+
+def pin_bf16_named_values():
+    """Values fixed by the bf16 format definition (sign, 8-bit exponent bias 127, 7-bit mantissa)."""
+    named = {0x3F80: 1.0, 0xC000: -2.0, 0x3FC0: 1.5, 0x0000: 0.0, 0x7F7F: (2.0 - 2.0 ** -7) * 2.0 ** 127,
+             0x0080: 2.0 ** -126, 0x0001: 2.0 ** -133, 0x4049: 3.140625}
+    for b, v in named.items():
+        assert float(oracle.bf16.decode(np.array([b]))[0]) == v, hex(b)
+    assert np.signbit(oracle.bf16.decode(np.array([0x8000]))[0])
+
+
+def pin_quant_bf16_matches_widened(seed=31):
+    """The bf16 quantizer equals the fp32 quantizer on the exactly widened values (bit for bit),
+    and on bf16 data that is exactly representable its scale follows the one-hot closed form."""
+    rng = np.random.default_rng(seed)
+    x = (rng.standard_normal((8, 256)) * 3).astype(np.float32)
+    bits = (x.view(np.uint32) >> np.uint32(16)).astype(np.uint16)      # truncation: still valid bf16 data
+    widened = (bits.astype(np.uint32) << np.uint32(16)).view(np.float32)
+    q1, s1 = oracle.quant.quantize_per_token_group_bf16(bits)
+    q2, s2 = oracle.quant.quantize_per_token_group(widened)
+    assert np.array_equal(q1, q2) and np.array_equal(s1.view(np.uint32), s2.view(np.uint32))
+    one = np.zeros((1, 128), np.uint16)
+    one[0, 5] = 0xC2E0                                                  # -112.0
+    q, s = oracle.quant.quantize_per_token_group_bf16(one)
+    assert s[0, 0] == np.float32(112.0) / np.float32(448.0) and q[0, 5] == 0xFE and q[0].sum() == 0xFE
+
+
 ALL_PINS = [
     pin_e4m3_named_codes, pin_e4m3_decode_vs_torch, pin_e4m3_roundtrip, pin_e4m3_encode_vs_torch,
     pin_e4m3_ties_and_saturation, pin_e4m3_brute_force_sample,
@@ -441,4 +476,5 @@ ALL_PINS = [
     pin_quant_pow2_invariance, pin_quant_zero_group, pin_quant_block_edges,
     pin_gemm_exact_rational, pin_gemm_all_448, pin_gemm_hadamard, pin_gemm_one_hot,
     pin_gemm_invariants, pin_gemm_grouped,
+    pin_bf16_decode_vs_torch, pin_bf16_named_values, pin_quant_bf16_matches_widened,
 ]

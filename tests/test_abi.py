@@ -72,6 +72,10 @@ def test_argument_validation(lib):
     assert lib.dg_quantize_per_token_group(mis, 1, 4, 128, fake, fake, 4, None) == DG_ERR_INVALID_ARG
     assert lib.dg_quantize_per_token_group(None, 1, 0, 128, None, None, 0, None) == DG_OK       # empty
     assert lib.dg_quantize_per_token_group(None, 0, 4, 128, None, None, 4, None) == DG_OK
+    assert lib.dg_quantize_per_token_group_bf16(fake, 1, 4, 100, fake, fake, 4, None) == DG_ERR_INVALID_ARG
+    assert lib.dg_quantize_per_token_group_bf16(fake, 1, 5, 128, fake, fake, 4, None) == DG_ERR_INVALID_ARG
+    assert lib.dg_quantize_per_token_group_bf16(mis, 1, 4, 128, fake, fake, 4, None) == DG_ERR_INVALID_ARG
+    assert lib.dg_quantize_per_token_group_bf16(None, 1, 0, 128, None, None, 0, None) == DG_OK
     assert lib.dg_quantize_per_block(fake, 1, 10, 130, fake, fake, None) == DG_ERR_INVALID_ARG
     assert lib.dg_quantize_per_block(None, 1, 10, 128, fake, fake, None) == DG_ERR_INVALID_ARG
     assert lib.dg_quantize_per_block(None, 0, 10, 128, None, None, None) == DG_OK

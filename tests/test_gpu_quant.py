@@ -196,3 +196,65 @@ def test_token_group_batched():
         qo, so = oracle.quant.quantize_per_token_group(x[g])
         assert np.array_equal(q[g], qo)
         assert np.array_equal(bits32(sa[g, :, :77].T), bits32(so))
+
+
+def run_token_group_bf16(bits, ld_extra=0):
+    """bf16 bits (M, K) or (G, M, K) -> GPU (q, sa) via the bf16 entry point."""
+    xd = torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).to(device()).view(torch.bfloat16)
+    m, k = bits.shape[-2:]
+    ld = dg.dg_get_scale_ld(m) + ld_extra
+    lead = bits.shape[:-2]
+    sa = torch.full(lead + (k // 128, ld), float("nan"), dtype=torch.float32, device=device())
+    q, sa = dg.dg_quantize_per_token_group(xd, sa=sa)
+    torch.cuda.synchronize()
+    sa_np = sa.cpu().numpy()
+    if ld > m:
+        assert np.all(np.isnan(sa_np[..., m:]))
+    return q.cpu().numpy(), sa_np[..., :m]
+
+
+@pytest.mark.parametrize("m,k,ld_extra", [(128, 512, 0), (1, 128, 0), (77, 384, 4), (1000, 640, 0),
+                                          (4096, 7168, 0)])
+def test_token_group_bf16_bit_exact(m, k, ld_extra):
+    """bf16 activations (N(0,1) with 1% outlier rows, rounded to bf16): bit-exact against the
+    oracle on the same bf16 values."""
+    say("quant token group bf16", m, k)
+    rng = inputs.rng_for("quant_bf16", m, k)
+    bits = inputs.to_bf16_bits(inputs.activations_with_outliers(rng, m, k) if m > 1 else inputs.normal(rng, (m, k)))
+    q, s = run_token_group_bf16(bits, ld_extra)
+    qo, so = oracle_quant_rows(oracle.bf16.decode(bits)) if m >= 512 else \
+        oracle.quant.quantize_per_token_group_bf16(bits)
+    assert np.array_equal(bits32(s.T), bits32(so))
+    assert np.array_equal(q, qo)
+
+
+def test_token_group_bf16_special_values():
+    """Extreme bf16 inputs: the largest finite value, the smallest subnormal, signed zeros,
+    groups of one magnitude, an all-zero group."""
+    say("quant token group bf16 special values")
+    rng = np.random.default_rng(41)
+    bits = rng.integers(0, 1 << 16, size=(6, 512)).astype(np.uint16)
+    bits &= np.uint16(0x7F7F) | np.uint16(0x8000)            # finite patterns only (exponent < 255)
+    bits[0, :128] = 0x7F7F                                    # max finite
+    bits[0, 128:256] = 0xFF7F                                 # -max finite
+    bits[1, :] = 0x0001                                       # smallest subnormal everywhere
+    bits[2, :128] = 0x8000                                    # -0.0 group
+    bits[2, 128:256] = 0x0000                                 # +0.0 group
+    bits[3, 5] = 0x7F7F                                       # one huge value among random ones
+    q, s = run_token_group_bf16(bits)
+    qo, so = oracle.quant.quantize_per_token_group_bf16(bits)
+    assert np.array_equal(bits32(s.T), bits32(so))
+    assert np.array_equal(q, qo)
+
+
+def test_token_group_bf16_batched_matches_fp32():
+    """(G, M, K) bf16 input gives the bytes and scales of the fp32 entry point on the widened values."""
+    say("quant token group bf16 batched")
+    rng = inputs.rng_for("quant_bf16_batched")
+    bits = inputs.to_bf16_bits(inputs.normal(rng, (3, 40, 384)) * np.float32(7.0))
+    q16, s16 = run_token_group_bf16(bits, ld_extra=4)
+    widened = oracle.bf16.decode(bits)
+    q32, s32 = dg.dg_quantize_per_token_group(to_dev(widened))
+    torch.cuda.synchronize()
+    assert np.array_equal(q16, q32.cpu().numpy())
+    assert np.array_equal(bits32(s16), bits32(s32.cpu().numpy()[..., :40]))

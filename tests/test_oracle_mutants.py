@@ -12,6 +12,7 @@ import oracle_pins
 E = oracle.e4m3
 Q = oracle.quant
 G = oracle.gemm
+B = oracle.bf16
 
 _orig_encode = E.encode
 _orig_decode = E.decode
@@ -114,6 +115,18 @@ def _masked_no_clamp_computes_all(qa, sa, qb, sb, masked_m):
     return _orig_masked(qa, sa, qb, sb, np.full(len(masked_m), np.asarray(qa).shape[1]))
 
 
+_orig_bf16_decode = B.decode
+
+
+def _bf16_decode_drops_sign(bits):
+    return np.abs(_orig_bf16_decode(bits))
+
+
+def _bf16_decode_shift8(bits):
+    b = np.asarray(bits).astype(np.uint32) & np.uint32(0xFFFF)
+    return (b << np.uint32(8)).view(np.float32)
+
+
 MUTANTS = {
     "encode_ties_away": (E, "encode", _encode_half_away),
     "encode_no_saturation": (E, "encode", _encode_no_saturation),
@@ -128,6 +141,8 @@ MUTANTS = {
     "gemm_act_scale_kb_reversed": (G, "gemm_nt", _gemm_sa_reversed_kb),
     "contiguous_expert_off_by_one": (G, "gemm_grouped_contiguous", _contig_off_by_one),
     "masked_writes_all_rows": (G, "gemm_grouped_masked", _masked_no_clamp_computes_all),
+    "bf16_decode_drops_sign": (B, "decode", _bf16_decode_drops_sign),
+    "bf16_decode_shift8": (B, "decode", _bf16_decode_shift8),
 }
 
 
