@@ -7,9 +7,9 @@ is not built, every call raises - there is no fallback.
 
 Functions carry the C names:
 
-* ``dg_quantize_per_token_group(x)``  -> (q uint8 (M, K), sa float32 (K/128, ld_sa)); fp32 or
+* ``dg_quantize_per_token_group(x)``  -> (q uint8 (M, K), sa float32 (ceil(K/128), ld_sa)); fp32 or
   bf16 x (the bf16 entry point is ``dg_quantize_per_token_group_bf16``)
-* ``dg_quantize_per_block(w)``        -> (q uint8 like w, sb float32 ([G,] ceil(N/128), K/128))
+* ``dg_quantize_per_block(w)``        -> (q uint8 like w, sb float32 ([G,] ceil(N/128), ceil(K/128)))
 * ``dg_gemm_fp8_nt(a, sa, b, sb)``    -> d bf16 (M, N)
 * ``dg_gemm_fp8_grouped_contiguous(a, sa, b, sb, m_indices)``  -> d bf16 (M_total, N)
 * ``dg_gemm_fp8_grouped_masked(a, sa, b, sb, masked_m)``       -> d bf16 (G, M_max, N)
@@ -171,7 +171,7 @@ def dg_quantize_per_token_group(x, q=None, sa=None):
              "x must be float32 or bfloat16, (M, K) or (G, M, K)")
     grouped = x.dim() == 3
     g, m, k = (x.shape if grouped else (1,) + tuple(x.shape))
-    kb = k // 128 if k % 128 == 0 else 0
+    kb = -(-k // 128)   # a last K group of k % 128 elements is partial
     if q is None:
         q = torch.empty(x.shape, dtype=torch.uint8, device=x.device)
     if sa is None:
@@ -195,7 +195,7 @@ def dg_quantize_per_block(w, q=None, sb=None):
     _require(w.dtype == torch.float32 and w.dim() in (2, 3), "w must be float32 (N, K) or (G, N, K)")
     grouped = w.dim() == 3
     g, n, k = (w.shape if grouped else (1,) + tuple(w.shape))
-    nb, kb = -(-n // 128), max(k // 128, 1)
+    nb, kb = -(-n // 128), max(-(-k // 128), 1)
     if q is None:
         q = torch.empty(w.shape, dtype=torch.uint8, device=w.device)
     if sb is None:

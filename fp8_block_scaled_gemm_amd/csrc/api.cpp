@@ -105,7 +105,7 @@ int dg_get_m_alignment_for_contiguous_layout(void) { return kGroup; }
 int64_t dg_get_scale_ld(int64_t rows) { return rows <= 0 ? 0 : (rows + 3) / 4 * 4; }
 
 size_t dg_gemm_workspace_size(int64_t m, int64_t n, int64_t k, int64_t num_groups) {
-  if (m <= 0 || n <= 0 || k <= 0 || k % kGroup || num_groups <= 0) return 0;
+  if (m <= 0 || n <= 0 || k <= 0 || k % kKAlign || num_groups <= 0) return 0;
   const int cus = effective_cus();
   if (cus < 0) return 0;
   return gemm_workspace_size(m, n, k, num_groups, cus);
@@ -113,8 +113,8 @@ size_t dg_gemm_workspace_size(int64_t m, int64_t n, int64_t k, int64_t num_group
 
 static int check_token_group(const void* x, int64_t num_groups, int64_t m, int64_t k, uint8_t* q, float* sa,
                              int64_t ld_sa) {
-  DG_REQUIRE(num_groups >= 0 && m >= 0 && k > 0 && k % kGroup == 0,
-             "quantize_per_token_group: need groups >= 0, m >= 0, k > 0, k %% 128 == 0 (m=%lld k=%lld)",
+  DG_REQUIRE(num_groups >= 0 && m >= 0 && k > 0 && k % kKAlign == 0,
+             "quantize_per_token_group: need groups >= 0, m >= 0, k > 0, k %% 16 == 0 (m=%lld k=%lld)",
              (long long)m, (long long)k);
   DG_REQUIRE(ld_sa >= m && ld_sa % 4 == 0, "quantize_per_token_group: need ld_sa >= m and ld_sa %% 4 == 0 (ld_sa=%lld)",
              (long long)ld_sa);
@@ -140,8 +140,8 @@ int dg_quantize_per_token_group_bf16(const uint16_t* x, int64_t num_groups, int6
 
 int dg_quantize_per_block(const float* w, int64_t num_groups, int64_t n, int64_t k, uint8_t* q,
                           float* sb, dg_stream_t stream) {
-  DG_REQUIRE(num_groups >= 0 && n >= 0 && k > 0 && k % kGroup == 0,
-             "quantize_per_block: need groups >= 0, n >= 0, k > 0, k %% 128 == 0");
+  DG_REQUIRE(num_groups >= 0 && n >= 0 && k > 0 && k % kKAlign == 0,
+             "quantize_per_block: need groups >= 0, n >= 0, k > 0, k %% 16 == 0");
   if (num_groups == 0 || n == 0) return DG_OK;
   DG_REQUIRE(w && q && sb, "quantize_per_block: null pointer");
   DG_REQUIRE(aligned16(w) && aligned16(q) && aligned16(sb), "quantize_per_block: pointers must be 16-byte aligned");
@@ -150,7 +150,7 @@ int dg_quantize_per_block(const float* w, int64_t num_groups, int64_t n, int64_t
 
 static int check_gemm_common(const uint8_t* a, const float* sa, int64_t ld_sa, const uint8_t* b,
                              const float* sb, uint16_t* d, int64_t rows, int64_t n, int64_t k) {
-  DG_REQUIRE(rows >= 0 && n >= 0 && k > 0 && k % kGroup == 0, "gemm: need m >= 0, n >= 0, k > 0, k %% 128 == 0 (m=%lld n=%lld k=%lld)",
+  DG_REQUIRE(rows >= 0 && n >= 0 && k > 0 && k % kKAlign == 0, "gemm: need m >= 0, n >= 0, k > 0, k %% 16 == 0 (m=%lld n=%lld k=%lld)",
              (long long)rows, (long long)n, (long long)k);
   DG_REQUIRE(ld_sa >= rows && ld_sa % 4 == 0, "gemm: need ld_sa >= m and ld_sa %% 4 == 0 (ld_sa=%lld m=%lld)",
              (long long)ld_sa, (long long)rows);
@@ -211,7 +211,7 @@ int dg_gemm_fp8_grouped_masked(const uint8_t* a, const float* sa, int64_t ld_sa,
 const char* dg_gemm_config_name(int layout, int64_t m, int64_t n, int64_t k, int64_t num_groups) {
   static thread_local char buf[96];
   buf[0] = 0;
-  if (layout < 0 || layout > 2 || m <= 0 || n <= 0 || k <= 0 || k % kGroup || num_groups <= 0) return buf;
+  if (layout < 0 || layout > 2 || m <= 0 || n <= 0 || k <= 0 || k % kKAlign || num_groups <= 0) return buf;
   const int cus = effective_cus();
   if (cus < 0) return buf;
   gemm_config_name(layout, m, n, k, num_groups, cus, buf, sizeof(buf));

@@ -12,6 +12,7 @@ typedef int v8i __attribute__((ext_vector_type(8)));
 typedef float v4f __attribute__((ext_vector_type(4)));
 
 constexpr int kGroup = 128;     // K-group / scale-block edge (fine-grained scaling granularity)
+constexpr int kKAlign = 16;     // K must be a multiple of this (16-byte rows); a last K group may be partial
 constexpr float kE4M3Max = 448.0f;
 
 // Status codes mirror include/dg.h.

@@ -216,7 +216,8 @@ __global__ __launch_bounds__(C::kThreads) void gemm_fp8_kernel(GemmParams p) {
     constexpr int kBandRows = 8 * C::kWaves;
     constexpr int kBandsB = C::kDmaB / C::kWaves;
     const int dma_row = 8 * wave + (lane >> 3);   // tile-local row within band 0 (f(row) is band-invariant)
-    const uint32_t dma_off = (uint32_t)dma_row * (uint32_t)p.k + (uint32_t)(((lane & 7) ^ swz_row(dma_row)) << 4);
+    const int dma_chunk = ((lane & 7) ^ swz_row(dma_row)) << 4;   // byte offset of this lane's chunk in the K block
+    const uint32_t dma_off = (uint32_t)dma_row * (uint32_t)p.k + (uint32_t)dma_chunk;
     const uint32_t band_step = (uint32_t)kBandRows * (uint32_t)p.k;
     const __amdgpu_buffer_rsrc_t rs_b =
         make_rsrc(b_g + (int64_t)n0 * p.k, p.n > n0 ? (int64_t)(p.n - n0) * p.k : 0);
@@ -256,12 +257,17 @@ __global__ __launch_bounds__(C::kThreads) void gemm_fp8_kernel(GemmParams p) {
       // of the band-0 offset, rather than kept live in a register per band across the main loop
       uint32_t base_off = dma_off;
       asm volatile("" : "+v"(base_off));
+      // a partial last K block (k % 128 != 0): chunks past k take an out-of-range offset, so the
+      // range check writes zeros instead of reading the next row's bytes
+      const bool tail = (kb + 1) * kGroup > p.k;   // wave-uniform
+      const bool chunk_out = tail && kb * kGroup + dma_chunk >= p.k;
 #pragma unroll
       for (int u = 0; u < C::kDmaPerWave; ++u) {
         const int q = wave + C::kWaves * u;
         const bool is_b = u < kBandsB;
-        lds_dma16(is_b ? rs_b : rs_a, sbase + q * (C::kDmaRows * kGroup),
-                  base_off + (uint32_t)(is_b ? u : u - kBandsB) * band_step, kb * kGroup);
+        const uint32_t voff = base_off + (uint32_t)(is_b ? u : u - kBandsB) * band_step;
+        lds_dma16(is_b ? rs_b : rs_a, sbase + q * (C::kDmaRows * kGroup), chunk_out ? 0xFFFFFFF0u : voff,
+                  kb * kGroup);
       }
       if (sa_active)
         lds_dma16(rs_sa, sbase + C::kSaOffset + 16 * wave * C::kSaLanesPerWave, sa_src, kb * (int)p.ld_sa * 4);
@@ -507,7 +513,7 @@ static void finish_plan(Plan& pl, int64_t m, int64_t n, int64_t k, int64_t group
   pl.tiles = (int64_t)pl.tiles_m * pl.tiles_n * groups;
   if (pl.tiles > kMaxCounterTiles) {   // one arrival counter per tile must fit the counter prefix
     pl.splits = 1;
-    pl.kb_per_split = (int)(k / kGroup);
+    pl.kb_per_split = (int)((k + kGroup - 1) / kGroup);
   }
   pl.ws_bytes = 0;
   if (pl.splits > 1) pl.ws_bytes = kCounterBytes + (size_t)pl.tiles * pl.splits * (size_t)li.bn * li.bm * 4;
@@ -552,7 +558,7 @@ static double decode_estimate(const LaunchInfo& li, int occ, int64_t m, int64_t 
 }
 
 static Plan make_decode_plan(int64_t m, int64_t n, int64_t k, int64_t groups, int num_cus, bool allow_split) {
-  const int kb_total = (int)(k / kGroup);
+  const int kb_total = (int)((k + kGroup - 1) / kGroup);
   Plan pl{};
   pl.cfg = m <= 64 ? kCfgDec64 : kCfgDec128;
   pl.splits = 1;
@@ -583,7 +589,7 @@ static Plan make_plan(int layout, int64_t m, int64_t n, int64_t k, int64_t group
   Plan pl{};
   pl.cfg = layout == kContiguous ? kCfgRows128 : choose_large(m, n, groups, num_cus);
   const LaunchInfo li = cfg_info<kDense>(pl.cfg);
-  const int kb_total = (int)(k / kGroup);
+  const int kb_total = (int)((k + kGroup - 1) / kGroup);
   pl.splits = 1;
   // few tiles and a long K (e.g. 256 x 512 x 8192): split K so that every CU gets work
   const int64_t tiles = ((m + li.bm - 1) / li.bm) * ((n + li.bn - 1) / li.bn) * groups;
@@ -645,12 +651,12 @@ int launch_gemm(int layout, const uint8_t* a, const float* sa, int64_t ld_sa, co
   p.ld_sa = ld_sa;
   p.m = (int)m; p.n = (int)n; p.k = (int)k;
   p.num_groups = (int)(layout == kDense ? 1 : groups);
-  p.kb_total = (int)(k / kGroup);
+  p.kb_total = (int)((k + kGroup - 1) / kGroup);
   p.nb128 = (int)((n + kGroup - 1) / kGroup);
   p.tiles_m = pl.tiles_m; p.tiles_n = pl.tiles_n;
   p.splits = pl.splits; p.kb_per_split = pl.kb_per_split;
   p.a_gstride = m * k;
-  p.sa_gstride = (k / kGroup) * ld_sa;
+  p.sa_gstride = (int64_t)p.kb_total * ld_sa;
   p.b_gstride = n * k;
   p.sb_gstride = (int64_t)p.nb128 * p.kb_total;
   p.d_gstride = m * n;

@@ -45,17 +45,19 @@ __global__ __launch_bounds__(kTokThreads) void quant_token_group_kernel(
   const int lane = threadIdx.x & 31;
   const int row = blockIdx.x * kTokRows + (threadIdx.x >> 5);   // stacked row: g * m + r
   if (row >= total_rows) return;                                 // uniform per half-wave
-  const int kbc = k / kGroup;
+  const int kbc = (k + kGroup - 1) / kGroup;   // a last group of k % 128 elements is partial
   const int kb0 = blockIdx.y * kTokKb;
   const int g = row / m, r = row - g * m;
   const T* src = x + (int64_t)row * k + kb0 * kGroup;
   uint8_t* dst = q + (int64_t)row * k + kb0 * kGroup;
   float* scl = sa + ((int64_t)g * kbc + kb0) * ld_sa + r;
 
+  // lane columns past k (partial last group) read as zeros: the amax is that of the elements present
   v4f v[kTokKb];
 #pragma unroll
   for (int u = 0; u < kTokKb; ++u)
-    if (kb0 + u < kbc) v[u] = load4(src + u * kGroup + 4 * lane);
+    v[u] = (kb0 + u < kbc && (kb0 + u) * kGroup + 4 * lane < k) ? load4(src + u * kGroup + 4 * lane)
+                                                                : v4f{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int u = 0; u < kTokKb; ++u) {
     if (kb0 + u >= kbc) break;   // uniform
@@ -64,7 +66,7 @@ __global__ __launch_bounds__(kTokThreads) void quant_token_group_kernel(
     const float s = amax == 0.0f ? 1.0f : amax / kE4M3Max;
     const uint32_t packed = pack4_e4m3(clamp448(v[u].x / s), clamp448(v[u].y / s),
                                        clamp448(v[u].z / s), clamp448(v[u].w / s));
-    reinterpret_cast<uint32_t*>(dst + u * kGroup)[lane] = packed;
+    if ((kb0 + u) * kGroup + 4 * lane < k) reinterpret_cast<uint32_t*>(dst + u * kGroup)[lane] = packed;
     if (lane == 0) scl[(int64_t)u * ld_sa] = s;
   }
 }
@@ -79,7 +81,7 @@ constexpr int kBlkThreads = 256;
 __global__ __launch_bounds__(kBlkThreads) void quant_block_kernel(
     const float* __restrict__ w, int64_t n, int64_t k, uint8_t* __restrict__ q,
     float* __restrict__ sb, int64_t nb_n) {
-  const int64_t kbc = k / kGroup;
+  const int64_t kbc = (k + kGroup - 1) / kGroup;
   const int64_t bid = blockIdx.x;
   const int64_t kb = bid % kbc;
   const int64_t t = bid / kbc;
@@ -91,6 +93,7 @@ __global__ __launch_bounds__(kBlkThreads) void quant_block_kernel(
   const int tid = threadIdx.x;
   const int c4 = tid & 31;
   const int r0 = tid >> 5;
+  const bool col_ok = kb * kGroup + 4 * c4 < k;   // a partial last K block: columns past k are absent
   const float* src = w + (g * n + row0) * k + kb * kGroup;
   uint8_t* dst = q + (g * n + row0) * k + kb * kGroup;
 
@@ -99,7 +102,7 @@ __global__ __launch_bounds__(kBlkThreads) void quant_block_kernel(
 #pragma unroll
   for (int u = 0; u < 16; ++u) {
     const int r = r0 + 8 * u;
-    if (r < rows_here) {
+    if (r < rows_here && col_ok) {
       v[u] = __builtin_nontemporal_load(reinterpret_cast<const v4f*>(src + r * k) + c4);
       amax = fmaxf(amax, fmaxf(fmaxf(fabsf(v[u].x), fabsf(v[u].y)), fmaxf(fabsf(v[u].z), fabsf(v[u].w))));
     }
@@ -114,7 +117,7 @@ __global__ __launch_bounds__(kBlkThreads) void quant_block_kernel(
 #pragma unroll
   for (int u = 0; u < 16; ++u) {
     const int r = r0 + 8 * u;
-    if (r < rows_here) {
+    if (r < rows_here && col_ok) {
       reinterpret_cast<uint32_t*>(dst + r * k)[c4] =
           pack4_e4m3(clamp448(v[u].x / s), clamp448(v[u].y / s), clamp448(v[u].z / s),
                      clamp448(v[u].w / s));
@@ -130,7 +133,7 @@ template <class T>
 static int launch_token_group(const T* x, int64_t mats, int64_t m, int64_t k, uint8_t* q, float* sa,
                               int64_t ld_sa, hipStream_t stream) {
   const int64_t total_rows = mats * m;
-  const int64_t kbc = k / kGroup;
+  const int64_t kbc = (k + kGroup - 1) / kGroup;
   if (total_rows > 0x7fffffffLL || k > 0x7fffffffLL)
     return set_error(kUnsupported, "quantize_per_token_group: more than 2^31 rows or columns");
   const int64_t gx = (total_rows + kTokRows - 1) / kTokRows;
@@ -156,7 +159,7 @@ int launch_quant_token_group_bf16(const uint16_t* x, int64_t mats, int64_t m, in
 int launch_quant_block(const float* w, int64_t groups, int64_t n, int64_t k, uint8_t* q, float* sb,
                        hipStream_t stream) {
   const int64_t nb_n = (n + kGroup - 1) / kGroup;
-  const int64_t blocks = groups * nb_n * (k / kGroup);
+  const int64_t blocks = groups * nb_n * ((k + kGroup - 1) / kGroup);
   if (blocks > 0x7fffffffLL) return set_error(kUnsupported, "quantize_per_block: too many blocks");
   hipLaunchKernelGGL(quant_block_kernel, dim3((unsigned)blocks), dim3(kBlkThreads), 0, stream, w,
                      n, k, q, sb, nb_n);

@@ -24,14 +24,18 @@
  *     aligned.
  *   - E4M3 means the OCP E4M3FN encoding (largest finite value 448).  FP8
  *     operands are passed as uint8_t bytes; bf16 outputs as uint16_t bits.
- *   - K (the reduction length) must be a positive multiple of 128.
+ *   - K (the reduction length) must be a positive multiple of 16 (16-byte rows).
+ *     KB = ceil(K / 128) scale groups cover it; when K % 128 != 0 the last group
+ *     holds the K % 128 elements present, its scale is their amax / 448, and the
+ *     GEMM treats the absent positions as zeros (the pages ask for irregular
+ *     shapes - ai.abqq.net summary, section 1 - without fixing this case).
  *   - Activation scales `sa` are stored K-group-major ("MN-major"):
  *     sa[kb * ld_sa + row] is the scale of row `row`, columns
- *     [128*kb, 128*kb+128).  ld_sa >= rows and ld_sa % 4 == 0
+ *     [128*kb, min(128*kb+128, K)).  ld_sa >= rows and ld_sa % 4 == 0
  *     (dg_get_scale_ld gives the smallest such value).
- *   - Weight scales `sb` are stored block-row-major: sb[nb * (k/128) + kb]
- *     is the scale of rows [128*nb, 128*nb+128) (a partial last block is
- *     allowed), columns [128*kb, 128*kb+128).
+ *   - Weight scales `sb` are stored block-row-major: sb[nb * KB + kb] is the
+ *     scale of rows [128*nb, 128*nb+128) (a partial last block is allowed),
+ *     columns [128*kb, min(128*kb+128, K)).
  *   - Work is enqueued on `stream` (a hipStream_t; NULL = the default
  *     stream) without any host synchronisation: device-resident counts
  *     (m_indices, masked_m) are read by the kernels only.
@@ -79,10 +83,10 @@ const char* dg_last_error_message(void);
  *   q    = E4M3 round-to-nearest-even, saturating, of fl32(x / s) (IEEE division)
  * x  : fp32 (num_groups, m, k) row-major, read only.
  * q  : E4M3 bytes (num_groups, m, k) row-major, written.
- * sa : fp32 scales, MN-major per group: written at sa[(g * (k/128) + kb) * ld_sa + r]
+ * sa : fp32 scales, MN-major per group: written at sa[(g * KB + kb) * ld_sa + r]
  *      for r < m; entries r >= m are untouched.
  * Errors: DG_ERR_INVALID_ARG for null/misaligned pointers, m < 0, num_groups < 0,
- * k % 128 != 0, ld_sa < m or ld_sa % 4 != 0.  Output is bit-exact (the result is unique).
+ * k % 16 != 0, ld_sa < m or ld_sa % 4 != 0.  Output is bit-exact (the result is unique).
  */
 int dg_quantize_per_token_group(const float* x, int64_t num_groups, int64_t m, int64_t k, uint8_t* q,
                                 float* sa, int64_t ld_sa, dg_stream_t stream);
@@ -104,9 +108,9 @@ int dg_quantize_per_token_group_bf16(const uint16_t* x, int64_t num_groups, int6
  * block at the N edge takes its amax over the rows present).
  * w  : fp32 (num_groups, n, k) row-major, read only.
  * q  : E4M3 bytes (num_groups, n, k), written.
- * sb : fp32 (num_groups, ceil(n/128), k/128), written.
+ * sb : fp32 (num_groups, ceil(n/128), KB), written.
  * Errors: DG_ERR_INVALID_ARG for null/misaligned pointers, n < 0, num_groups < 0,
- * k % 128 != 0.  Output is bit-exact.
+ * k % 16 != 0.  Output is bit-exact.
  */
 int dg_quantize_per_block(const float* w, int64_t num_groups, int64_t n, int64_t k, uint8_t* q,
                           float* sb, dg_stream_t stream);
@@ -117,7 +121,7 @@ int dg_quantize_per_block(const float* w, int64_t num_groups, int64_t n, int64_t
  * After every 128-deep K block the MFMA partial P is promoted into FP32
  * accumulators:  acc += P * fl32(sa[row, kb] * sb[n/128, kb]);  D = bf16_rne(acc).
  * a  : E4M3 (m, k) row-major.        sa : fp32, MN-major with stride ld_sa (see above).
- * b  : E4M3 (n, k) row-major.        sb : fp32 (ceil(n/128), k/128).
+ * b  : E4M3 (n, k) row-major.        sb : fp32 (ceil(n/128), KB).
  * d  : bf16 (m, n) row-major, written.
  * workspace : optional device scratch for split-K on small-m shapes.  Its first
  *   64 KiB hold per-tile arrival counters: they must be zero before the first
@@ -126,7 +130,7 @@ int dg_quantize_per_block(const float* w, int64_t num_groups, int64_t n, int64_t
  *   one stream (concurrent calls race).  NULL or too small (see
  *   dg_gemm_workspace_size) => no split-K: still correct, slower for small m.
  * Errors: DG_ERR_INVALID_ARG for null/misaligned pointers, negative sizes,
- * k % 128 != 0, ld_sa < m or ld_sa % 4 != 0.  Deterministic: the same inputs
+ * k % 16 != 0, ld_sa < m or ld_sa % 4 != 0.  Deterministic: the same inputs
  * give bit-identical outputs.
  */
 int dg_gemm_fp8_nt(const uint8_t* a, const float* sa, int64_t ld_sa, const uint8_t* b,
@@ -142,7 +146,7 @@ int dg_gemm_fp8_nt(const uint8_t* a, const float* sa, int64_t ld_sa, const uint8
  * A block whose index is outside [0, num_groups) (e.g. -1 padding) is skipped
  * and its D rows are left unwritten.
  * a  : E4M3 (m_total, k);  sa : fp32 MN-major, stride ld_sa >= m_total.
- * b  : E4M3 (num_groups, n, k);  sb : fp32 (num_groups, ceil(n/128), k/128).
+ * b  : E4M3 (num_groups, n, k);  sb : fp32 (num_groups, ceil(n/128), KB).
  * m_indices : int32 (m_total,), DEVICE memory, read by the kernel only.
  * d  : bf16 (m_total, n).
  * Errors: as dg_gemm_fp8_nt, plus m_total % 128 != 0.
@@ -157,8 +161,8 @@ int dg_gemm_fp8_grouped_contiguous(const uint8_t* a, const float* sa, int64_t ld
  * compute and skip invalid work such as empty decode tokens at run time).
  * For expert g only rows r < min(max(masked_m[g], 0), m_max) are computed and
  * written; rows at or past that count are never written.
- * a  : E4M3 (num_groups, m_max, k);  sa : fp32 (num_groups, k/128, ld_sa), ld_sa >= m_max.
- * b  : E4M3 (num_groups, n, k);      sb : fp32 (num_groups, ceil(n/128), k/128).
+ * a  : E4M3 (num_groups, m_max, k);  sa : fp32 (num_groups, KB, ld_sa), ld_sa >= m_max.
+ * b  : E4M3 (num_groups, n, k);      sb : fp32 (num_groups, ceil(n/128), KB).
  * d  : bf16 (num_groups, m_max, n).
  * masked_m : int32 (num_groups,), DEVICE memory, read by the kernel only.
  * workspace : as dg_gemm_fp8_nt (used for split-K when m_max is small).

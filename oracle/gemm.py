@@ -26,15 +26,19 @@ GROUP = 128
 
 
 def dequantize_rows(q, s):
-    """A' = dec(q) * s with q (R, K) codes and s (R, K/128) per-row group scales, fp64."""
+    """A' = dec(q) * s with q (R, K) codes and s (R, ceil(K/128)) per-row group scales, fp64.
+    A ragged last group (K mod 128 elements, reading O14) uses its own scale like the others."""
     q = np.asarray(q)
     r, k = q.shape
-    vals = e4m3.decode(q).reshape(r, k // GROUP, GROUP)
-    return (vals * np.asarray(s, dtype=np.float64)[:, :, None]).reshape(r, k)
+    kb = -(-k // GROUP)
+    vals = np.zeros((r, kb * GROUP))
+    vals[:, :k] = e4m3.decode(q)
+    vals = vals.reshape(r, kb, GROUP)
+    return (vals * np.asarray(s, dtype=np.float64)[:, :, None]).reshape(r, kb * GROUP)[:, :k]
 
 
 def dequantize_blocks(q, s):
-    """B' = dec(q) * s with q (N, K) codes and s (ceil(N/128), K/128) block scales, fp64."""
+    """B' = dec(q) * s with q (N, K) codes and s (ceil(N/128), ceil(K/128)) block scales, fp64."""
     q = np.asarray(q)
     n, k = q.shape
     row_scales = np.repeat(np.asarray(s, dtype=np.float64), GROUP, axis=0)[:n]

@@ -300,7 +300,7 @@ def pin_quant_block_edges(seed=17):
 
 def _random_operands(rng, m, n, k, g=None):
     codes = oracle.e4m3.all_finite_codes()
-    kb = k // 128
+    kb = -(-k // 128)
     qa = rng.choice(codes, size=(m, k)).astype(np.uint8)
     sa = np.exp2(rng.uniform(-8, 2, size=(m, kb))).astype(np.float32)
     shape_b = (n, k) if g is None else (g, n, k)
@@ -321,9 +321,9 @@ def exact_gemm(qa, sa, qb, sb):
         for j in range(n):
             tot = Fraction(0)
             tot_abs = Fraction(0)
-            for kb in range(k // 128):
+            for kb in range(-(-k // 128)):
                 scale = Fraction(float(sa[i, kb])) * Fraction(float(sb[j // 128, kb]))
-                for kk in range(128 * kb, 128 * kb + 128):
+                for kk in range(128 * kb, min(128 * kb + 128, k)):
                     t = _TABLE[int(qa[i, kk])] * _TABLE[int(qb[j, kk])] * scale
                     tot += t
                     tot_abs += abs(t)
@@ -469,6 +469,41 @@ def pin_quant_bf16_matches_widened(seed=31):
     assert s[0, 0] == np.float32(112.0) / np.float32(448.0) and q[0, 5] == 0xFE and q[0].sum() == 0xFE
 
 
+def pin_quant_ragged_k(seed=37):
+    """K not a multiple of 128 (reading O14): every group, the last one partial, against the scalar
+    brute force on exactly the elements present; weights too (a 128 x partial block)."""
+    rng = np.random.default_rng(seed)
+    for k in (16, 144, 400):
+        x = (rng.standard_normal((3, k)) * 5).astype(np.float32)
+        x[2, -16:] *= np.float32(1000.0)                # the partial group holds the row's outliers
+        q, sa = oracle.quant.quantize_per_token_group(x)
+        kb = -(-k // 128)
+        assert q.shape == (3, k) and sa.shape == (3, kb)
+        for m in range(3):
+            for g in range(kb):
+                bq, bs = brute_quantize_group(x[m, 128 * g:min(128 * g + 128, k)])
+                assert sa[m, g] == bs and np.array_equal(q[m, 128 * g:128 * g + len(bq)], bq), (k, m, g)
+        w = (rng.standard_normal((130, k)) * 0.1).astype(np.float32)
+        qw, sw = oracle.quant.quantize_per_block(w)
+        assert qw.shape == (130, k) and sw.shape == (2, kb)
+        last = w[128:, 128 * (kb - 1):]
+        bq, bs = brute_quantize_group(last.reshape(-1))
+        assert sw[1, kb - 1] == bs and np.array_equal(qw[128:, 128 * (kb - 1):].reshape(-1), bq)
+
+
+def pin_gemm_ragged_k_exact(seed=43):
+    """Ragged K: the fp64 oracle against exact rational arithmetic over the K elements present."""
+    rng = np.random.default_rng(seed)
+    m, n, k = 2, 131, 272          # K = 2 full groups + 16; N spans a partial block
+    qa, sa, qb, sb = _random_operands(rng, m, n, k)
+    got = oracle.gemm.gemm_nt(qa, sa, qb, sb)
+    ex, mag = exact_gemm(qa, sa, qb, sb)
+    for i in range(m):
+        for j in range(n):
+            bound = Fraction(k + 1) * Fraction(2) ** -53 * mag[i][j]
+            assert abs(Fraction(float(got[i, j])) - ex[i][j]) <= bound, (i, j)
+
+
 ALL_PINS = [
     pin_e4m3_named_codes, pin_e4m3_decode_vs_torch, pin_e4m3_roundtrip, pin_e4m3_encode_vs_torch,
     pin_e4m3_ties_and_saturation, pin_e4m3_brute_force_sample,
@@ -477,4 +512,5 @@ ALL_PINS = [
     pin_gemm_exact_rational, pin_gemm_all_448, pin_gemm_hadamard, pin_gemm_one_hot,
     pin_gemm_invariants, pin_gemm_grouped,
     pin_bf16_decode_vs_torch, pin_bf16_named_values, pin_quant_bf16_matches_widened,
+    pin_quant_ragged_k, pin_gemm_ragged_k_exact,
 ]

@@ -54,7 +54,7 @@ def test_pure_utilities(lib):
     assert lib.dg_status_string(DG_ERR_INVALID_ARG) == b"DG_ERR_INVALID_ARG"
     assert lib.dg_set_num_cus(0) == DG_ERR_INVALID_ARG
     assert b"n must be" in lib.dg_last_error_message()
-    assert lib.dg_gemm_workspace_size(64, 512, 100, 1) == 0   # k % 128 != 0: never split
+    assert lib.dg_gemm_workspace_size(64, 512, 100, 1) == 0   # k % 16 != 0: invalid, never split
 
 
 def _p(v):
@@ -81,7 +81,7 @@ def test_argument_validation(lib):
     assert lib.dg_quantize_per_block(None, 0, 10, 128, None, None, None) == DG_OK
     # dense GEMM
     args = lambda m, n, k, ld, a=fake, d=fake: (a, fake, ld, fake, fake, d, m, n, k, None, 0, None)
-    assert lib.dg_gemm_fp8_nt(*args(4, 8, 96, 4)) == DG_ERR_INVALID_ARG
+    assert lib.dg_gemm_fp8_nt(*args(4, 8, 100, 4)) == DG_ERR_INVALID_ARG        # k % 16 != 0
     assert lib.dg_gemm_fp8_nt(*args(4, 8, 0, 4)) == DG_ERR_INVALID_ARG
     assert lib.dg_gemm_fp8_nt(*args(8, 8, 128, 4)) == DG_ERR_INVALID_ARG          # ld_sa < m
     assert lib.dg_gemm_fp8_nt(*args(-1, 8, 128, 4)) == DG_ERR_INVALID_ARG

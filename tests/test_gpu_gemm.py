@@ -174,10 +174,11 @@ def masked_case(name, g, m_max, n, k, masked):
     b = inputs.grouped_weights(rng, g, n, k)
     qa, sa = oracle.quant.quantize_per_token_group(a.reshape(g * m_max, k))
     qa = qa.reshape(g, m_max, k)
-    sa = sa.reshape(g, m_max, k // 128)
+    kb = -(-k // 128)
+    sa = sa.reshape(g, m_max, kb)
     qb, sb = oracle.quant.quantize_per_block_grouped(b)
     ld = dg.dg_get_scale_ld(m_max)
-    sa_dev = np.zeros((g, k // 128, ld), np.float32)
+    sa_dev = np.zeros((g, kb, ld), np.float32)
     sa_dev[:, :, :m_max] = sa.transpose(0, 2, 1)
     d = torch.full((g, m_max, n), -1, dtype=torch.int16, device=device()).view(torch.bfloat16)
     masked = np.asarray(masked, np.int32)
@@ -212,3 +213,51 @@ def test_gemm_errors():
     sb = torch.zeros((1, 1), dtype=torch.float32, device=device())
     with pytest.raises(dg.DGError, match="INVALID_ARG"):
         dg.dg_gemm_fp8_nt(a, sa, b, sb)
+
+
+# ---- ragged K (K % 128 != 0, K % 16 == 0): the last K group is partial --------------------------
+
+@pytest.mark.parametrize("m,n,k", [(1, 32, 16), (64, 200, 144), (64, 512, 4112), (130, 260, 400),
+                                   (300, 1000, 1040), (33, 4096, 784), (257, 640, 2064)])
+def test_ragged_k(m, n, k):
+    """Dense GEMM with a partial last K group, across the decode (split and unsplit) and large
+    tile configurations; the absent K positions must contribute nothing."""
+    say("gemm ragged k", m, n, k, dg.dg_gemm_config_name(0, m, n, k))
+    qa, sa, qb, sb = quantized_operands("ragged_k", m, n, k)
+    check_gemm(run_dense(qa, sa, qb, sb, ld_extra=4), oracle.gemm.gemm_nt(qa, sa, qb, sb), f"ragged k {m}x{n}x{k}")
+
+
+def test_ragged_k_grouped():
+    """Contiguous and masked layouts with a partial last K group."""
+    say("gemm ragged k grouped")
+    masked_case("masked_ragged_k", 3, 128, 256, 400, [128, 5, 70])
+    rng = inputs.rng_for("contig_ragged_k")
+    n, k = 256, 272
+    sizes = np.array([129, 40], dtype=np.int64)
+    a, m_idx, valid = inputs.contiguous_activations(rng, sizes, k)
+    b = inputs.grouped_weights(rng, 2, n, k)
+    qa, sa = oracle.quant.quantize_per_token_group(a)
+    qb, sb = oracle.quant.quantize_per_block_grouped(b)
+    d = dg.dg_gemm_fp8_grouped_contiguous(to_dev(qa), sa_to_dev(sa), to_dev(qb), to_dev(sb), to_dev(m_idx))
+    torch.cuda.synchronize()
+    check_gemm(d, oracle.gemm.gemm_grouped_contiguous(qa, sa, qb, sb, m_idx), "contiguous ragged k")
+
+
+def test_ragged_k_from_gpu_quantizers():
+    """End to end on a partial last K group: the GPU quantizers' bytes equal the oracle's, and the
+    GEMM of them matches the oracle GEMM."""
+    say("gemm ragged k end to end")
+    m, n, k = 96, 384, 656
+    rng = inputs.rng_for("ragged_k_e2e")
+    a = inputs.activations_with_outliers(rng, m, k)
+    b = inputs.normal(rng, (n, k), 0.02)
+    qa_d, sa_d = dg.dg_quantize_per_token_group(to_dev(a))
+    qb_d, sb_d = dg.dg_quantize_per_block(to_dev(b))
+    d = dg.dg_gemm_fp8_nt(qa_d, sa_d, qb_d, sb_d)
+    torch.cuda.synchronize()
+    qa, sa = oracle.quant.quantize_per_token_group(a)
+    qb, sb = oracle.quant.quantize_per_block(b)
+    assert np.array_equal(qa_d.cpu().numpy(), qa) and np.array_equal(qb_d.cpu().numpy(), qb)
+    assert np.array_equal(sa_d.cpu().numpy()[:, :m].T.view(np.uint32), sa.view(np.uint32))
+    assert np.array_equal(sb_d.cpu().numpy().view(np.uint32), sb.view(np.uint32))
+    check_gemm(d, oracle.gemm.gemm_nt(qa, sa, qb, sb), "ragged k end to end")

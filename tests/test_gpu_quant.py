@@ -19,7 +19,7 @@ def run_token_group(x, ld_extra=0):
     m, k = x.shape
     xd = to_dev(x)
     ld = dg.dg_get_scale_ld(m) + ld_extra
-    sa = torch.full((k // 128, ld), float("nan"), dtype=torch.float32, device=device())
+    sa = torch.full((-(-k // 128), ld), float("nan"), dtype=torch.float32, device=device())
     q, sa = dg.dg_quantize_per_token_group(xd, sa=sa)
     torch.cuda.synchronize()
     sa_np = sa.cpu().numpy()
@@ -204,7 +204,7 @@ def run_token_group_bf16(bits, ld_extra=0):
     m, k = bits.shape[-2:]
     ld = dg.dg_get_scale_ld(m) + ld_extra
     lead = bits.shape[:-2]
-    sa = torch.full(lead + (k // 128, ld), float("nan"), dtype=torch.float32, device=device())
+    sa = torch.full(lead + (-(-k // 128), ld), float("nan"), dtype=torch.float32, device=device())
     q, sa = dg.dg_quantize_per_token_group(xd, sa=sa)
     torch.cuda.synchronize()
     sa_np = sa.cpu().numpy()
@@ -258,3 +258,30 @@ def test_token_group_bf16_batched_matches_fp32():
     torch.cuda.synchronize()
     assert np.array_equal(q16, q32.cpu().numpy())
     assert np.array_equal(bits32(s16), bits32(s32.cpu().numpy()[..., :40]))
+
+
+@pytest.mark.parametrize("m,k", [(3, 16), (77, 144), (130, 400), (8, 7184), (512, 2064)])
+def test_token_group_ragged_k(m, k):
+    """K % 128 != 0: the last group holds K mod 128 elements; its scale is their amax / 448."""
+    say("quant token group ragged k", m, k)
+    rng = inputs.rng_for("quant_ragged_k", m, k)
+    x = inputs.activations_with_outliers(rng, m, k) if m > 1 else inputs.normal(rng, (m, k))
+    x[:, -16:] *= np.float32(300.0)   # outliers inside the partial group
+    assert_token_group_exact(x)
+    bits = inputs.to_bf16_bits(x)
+    q, s = run_token_group_bf16(bits)
+    qo, so = oracle.quant.quantize_per_token_group_bf16(bits)
+    assert np.array_equal(bits32(s.T), bits32(so)) and np.array_equal(q, qo)
+
+
+@pytest.mark.parametrize("shape", [(130, 16), (256, 144), (2, 200, 400), (129, 2064)])
+def test_block_ragged_k(shape):
+    """K % 128 != 0: the last 128 x (K mod 128) block takes its amax over the columns present."""
+    say("quant block ragged k", shape)
+    rng = inputs.rng_for("quant_blk_ragged", *shape)
+    w = inputs.normal(rng, shape, 0.02)
+    w[..., -16:] *= np.float32(40.0)
+    q, sb = run_block(w)
+    qo, so = oracle.quant.quantize_per_block_grouped(w) if w.ndim == 3 else oracle.quant.quantize_per_block(w)
+    assert np.array_equal(bits32(sb), bits32(so))
+    assert np.array_equal(q, qo)

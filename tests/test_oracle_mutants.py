@@ -127,6 +127,30 @@ def _bf16_decode_shift8(bits):
     return (b << np.uint32(8)).view(np.float32)
 
 
+def _gemm_drops_k_tail(qa, sa, qb, sb):
+    """Ragged K handled by dropping the partial last group."""
+    k = np.asarray(qa).shape[1]
+    kf = k // 128 * 128
+    if kf == k:
+        return _orig_gemm_nt(qa, sa, qb, sb)
+    return _orig_gemm_nt(np.asarray(qa)[:, :kf], np.asarray(sa)[:, :kf // 128], np.asarray(qb)[:, :kf],
+                         np.asarray(sb)[:, :kf // 128])
+
+
+def _quant_tail_scale_from_full_window(x):
+    """Ragged K: the last group's scale taken over 128 elements wrapped from the row start."""
+    x = np.asarray(x, dtype=np.float32)
+    k = x.shape[1]
+    if k % 128 == 0:
+        return _orig_tok(x)
+    wrapped = np.concatenate([x, x[:, :128 - k % 128]], axis=1)
+    q, s = _orig_tok(wrapped)
+    return q[:, :k], s
+
+
+_orig_gemm_nt = G.gemm_nt
+_orig_tok = Q.quantize_per_token_group
+
 MUTANTS = {
     "encode_ties_away": (E, "encode", _encode_half_away),
     "encode_no_saturation": (E, "encode", _encode_no_saturation),
@@ -143,6 +167,8 @@ MUTANTS = {
     "masked_writes_all_rows": (G, "gemm_grouped_masked", _masked_no_clamp_computes_all),
     "bf16_decode_drops_sign": (B, "decode", _bf16_decode_drops_sign),
     "bf16_decode_shift8": (B, "decode", _bf16_decode_shift8),
+    "gemm_drops_ragged_k_tail": (G, "gemm_nt", _gemm_drops_k_tail),
+    "quant_ragged_tail_wrapped_scale": (Q, "quantize_per_token_group", _quant_tail_scale_from_full_window),
 }
 
 
