@@ -51,10 +51,12 @@ def parse():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="dense_v3",
-                    choices=["dense_v3", "small", "contiguous", "masked", "large_dense", "zipf"])
+                    choices=["dense_v3", "small", "contiguous", "masked", "large_dense", "zipf", "overlap"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target CPU work of the oracle sample")
     ap.add_argument("--eager", action="store_true", help="time eager launches instead of graph replays")
+    ap.add_argument("--num-cus", type=int, default=0,
+                    help="cap the GEMMs' persistent grid to this many CUs (dg_set_num_cus; 0 = all)")
     ap.add_argument("--act-dtype", default="fp32", choices=["fp32", "bf16"],
                     help="activation input type of the dense workloads (bf16: the bf16-input quantizer)")
     ap.add_argument("--spin-ms", type=float, default=20.0,
@@ -277,6 +279,79 @@ def cpu_baseline(workload, seconds):
 
 # ---------------------------------------------------------------------------
 
+def cu_masked_stream(torch, first, count, total):
+    """A HIP stream whose kernels may only run on CUs [first, first + count) (hipExtStreamCreateWithCUMask;
+    default priority), wrapped for torch."""
+    import ctypes
+    hip = ctypes.CDLL("libamdhip64.so")
+    words = (total + 31) // 32
+    mask = [0] * words
+    for cu in range(first, first + count):
+        mask[cu // 32] |= 1 << (cu % 32)
+    arr = (ctypes.c_uint32 * words)(*mask)
+    handle = ctypes.c_void_p()
+    err = hip.hipExtStreamCreateWithCUMask(ctypes.byref(handle), ctypes.c_uint32(words), arr)
+    if err != 0:
+        raise RuntimeError(f"hipExtStreamCreateWithCUMask failed ({err})")
+    return torch.cuda.ExternalStream(handle.value, device=torch.device("cuda", 0))
+
+
+def overlap_bench(args, torch, dg, dev):
+    """Comm-overlap mode (the CU cap beside a communication kernel, on one GPU): the prefill GEMM
+    4096 x 7168 x 16384 runs on a stream masked to the first C CUs with its persistent grid capped
+    to C (dg_set_num_cus), while a device copy standing in for an all-to-all runs on a stream
+    masked to the remaining CUs.  Times each alone and both together."""
+    cus = torch.cuda.get_device_properties(dev).multi_processor_count
+    c = args.num_cus if args.num_cus > 0 else cus - 32
+    dg.dg_set_num_cus(c)
+    m, n, k = 4096, 7168, 16384
+    gen = Gen(torch, dev, 77)
+    qa, sa = dg.dg_quantize_per_token_group(gen.activations(m, k))
+    qb, sb = dg.dg_quantize_per_block(gen.normal((n, k), 0.02))
+    d = torch.empty((m, n), dtype=torch.bfloat16, device=dev)
+    src = torch.empty(512 << 20, dtype=torch.uint8, device=dev).fill_(1)
+    dst = torch.empty_like(src)
+    s_gemm = cu_masked_stream(torch, 0, c, cus)
+    s_comm = cu_masked_stream(torch, c, cus - c, cus)
+    reps = max(args.steps, 5)
+
+    def run(gemm, comm):
+        torch.cuda.synchronize()
+        e = {}
+        for name, st, on, fn in (("gemm", s_gemm, gemm, lambda: dg.dg_gemm_fp8_nt(qa, sa, qb, sb, d=d)),
+                                 ("comm", s_comm, comm, lambda: dst.copy_(src))):
+            if not on:
+                continue
+            with torch.cuda.stream(st):
+                e[name] = [torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)]
+                fn()   # warm
+                e[name][0].record()
+                for _ in range(reps):
+                    fn()
+                e[name][1].record()
+        torch.cuda.synchronize()
+        return {kk: v[0].elapsed_time(v[1]) / reps for kk, v in e.items()}
+
+    run(True, True)
+    alone_g = run(True, False)["gemm"]
+    alone_c = run(False, True)["comm"]
+    both = run(True, True)
+    flops = 2.0 * m * n * k
+    copy_bytes = 2.0 * src.numel()
+    out = {"metric": METRIC, "value": round(flops / (both["gemm"] * 1e-3) / 1e12, 2), "unit": "TFLOP/s",
+           "n_gpus": 1, "steps": reps, "warmup": 1, "ms_per_step": round(both["gemm"], 4), "higher_is_better": True,
+           "scaling": "weak", "vs_baseline": None, "dtype": "fp8_e4m3", "data": "synthetic",
+           "config": {"workload": "overlap", "gemm": f"{m}x{n}x{k}", "gemm_cus": c, "comm_cus": cus - c,
+                      "gemm_config": dg.dg_gemm_config_name(0, m, n, k),
+                      "comm_stand_in": "512 MiB device copy (read + write) on a CU-masked stream"},
+           "overlap": {"gemm_alone_ms": round(alone_g, 4), "gemm_with_comm_ms": round(both["gemm"], 4),
+                       "gemm_alone_tflops": round(flops / (alone_g * 1e-3) / 1e12, 1),
+                       "comm_alone_gbps": round(copy_bytes / (alone_c * 1e-3) / 1e9, 1),
+                       "comm_with_gemm_gbps": round(copy_bytes / (both["comm"] * 1e-3) / 1e9, 1)},
+           "roofline": None, "cpu_baseline": None}
+    print(json.dumps(out), flush=True)
+
+
 def source_digest():
     """sha256 of the GEMM kernel source: traffic counters are only valid for the kernel they measured."""
     import hashlib
@@ -331,6 +406,11 @@ def main():
         copy_calibration(torch, dev)
         return
     dg.lib()
+    if args.num_cus > 0:
+        dg.dg_set_num_cus(args.num_cus)
+    if args.workload == "overlap":
+        overlap_bench(args, torch, dg, dev)
+        return
     ops, desc = build_workload(args.workload, torch, dg, dev, args.act_dtype)
     torch.cuda.synchronize()
     print(f"[bench] workload {args.workload}: {len(ops)} ops per step", file=sys.stderr, flush=True)

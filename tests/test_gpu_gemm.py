@@ -261,3 +261,32 @@ def test_ragged_k_from_gpu_quantizers():
     assert np.array_equal(sa_d.cpu().numpy()[:, :m].T.view(np.uint32), sa.view(np.uint32))
     assert np.array_equal(sb_d.cpu().numpy().view(np.uint32), sb.view(np.uint32))
     check_gemm(d, oracle.gemm.gemm_nt(qa, sa, qb, sb), "ragged k end to end")
+
+
+# ---- CU cap (dg_set_num_cus): the persistent grid leaves CUs free for other kernels -------------
+
+@pytest.mark.parametrize("cap", [1, 7, 64, 200])
+def test_cu_cap(cap):
+    """Every form stays correct with the grid capped to `cap` CUs (plans and K splits change
+    with the cap); a capped call whose plan equals the uncapped one is bit-identical to it."""
+    say("gemm cu cap", cap)
+    full = dg.dg_get_num_cus()
+    cases = [(64, 512, 4096), (300, 1000, 1024), (128, 256, 2048)]
+    try:
+        for (m, n, k) in cases:
+            qa, sa, qb, sb = quantized_operands("cucap", m, n, k)
+            name_full = dg.dg_gemm_config_name(0, m, n, k)
+            d_full = run_dense(qa, sa, qb, sb)
+            dg.dg_set_num_cus(cap)
+            assert dg.dg_get_num_cus() == min(cap, full)
+            name_cap = dg.dg_gemm_config_name(0, m, n, k)
+            d_cap = run_dense(qa, sa, qb, sb)
+            dg.dg_set_num_cus(full)
+            check_gemm(d_cap, oracle.gemm.gemm_nt(qa, sa, qb, sb), f"cap {cap} {m}x{n}x{k} ({name_cap})")
+            if name_cap == name_full:
+                assert np.array_equal(bf16_bits(d_cap), bf16_bits(d_full))
+        dg.dg_set_num_cus(cap)
+        masked_case("masked_cap", 4, 64, 256, 2048, [64, 7, 0, 33])
+        test_contiguous_small()
+    finally:
+        dg.dg_set_num_cus(full)
