@@ -20,10 +20,13 @@ news/blog pages; each function cites the page title and section it follows):
 * ``gemm``  - the three GEMM forms the pages list (normal, contiguous-grouped,
   masked-grouped: 机器之心 report, "quick start"; ai.abqq.net summary, section 3;
   3loumao explainer, section 03): dequantise exactly and multiply in fp64.
+* ``train`` - the backward GEMMs of a linear layer (the pages say the library serves V3/R1
+  training; the layouts are readings): per-channel token groups, transposed block scales and
+  the GEMM whose two operands both carry per-row group scales.
 
 Every function here is pinned by ``tests/test_oracle_*.py`` against facts that
 do not come from this package (the format definition, torch's independent
 float8_e4m3fn codec, exact rational arithmetic, closed forms, invariants).
 """
 
-from . import bf16, e4m3, quant, gemm  # noqa: F401
+from . import bf16, e4m3, quant, gemm, train  # noqa: F401

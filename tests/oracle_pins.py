@@ -504,6 +504,129 @@ def pin_gemm_ragged_k_exact(seed=43):
             assert abs(Fraction(float(got[i, j])) - ex[i][j]) <= bound, (i, j)
 
 
+# --------------------------------------------------------------------------
+# Training-side layouts (per-channel token groups, transposed blocks, row-scaled GEMM)
+# --------------------------------------------------------------------------
+
+
+def pin_channel_quant_brute_force(seed=47):
+    """Every 128-token group of every column, by the scalar brute-force group quantizer; M ragged
+    (200 = 128 + 72), columns of very different magnitudes, one all-zero column."""
+    rng = np.random.default_rng(seed)
+    m, k = 200, 5
+    x = (rng.standard_normal((m, k)) * np.array([1e-3, 1.0, 37.0, 0.0, 5e2])).astype(np.float32)
+    x[3, 1] = np.float32(-0.0)
+    qt, st = oracle.train.quantize_per_channel_group(x)
+    assert qt.shape == (k, m) and st.shape == (k, 2)
+    for col in range(k):
+        for b, (r0, r1) in enumerate(((0, 128), (128, m))):
+            q_ref, s_ref = brute_quantize_group(x[r0:r1, col])
+            assert st[col, b] == s_ref, (col, b)
+            assert np.array_equal(qt[col, r0:r1], q_ref), (col, b)
+
+
+def pin_channel_quant_is_token_quant_of_transpose(seed=53):
+    """Grouping 128 tokens of a column is grouping 128 elements of a row of x^T: the per-channel
+    quantizer must agree with the (separately pinned) per-token-group quantizer on x^T."""
+    rng = np.random.default_rng(seed)
+    x = (rng.standard_normal((272, 48)) * np.exp2(rng.uniform(-6, 6, size=(1, 48)))).astype(np.float32)
+    qt, st = oracle.train.quantize_per_channel_group(x)
+    q_ref, s_ref = oracle.quant.quantize_per_token_group(np.ascontiguousarray(x.T))
+    assert np.array_equal(qt, q_ref) and np.array_equal(st.view(np.uint32), s_ref.view(np.uint32))
+
+
+def pin_channel_quant_bf16_widening(seed=59):
+    """The bf16 variant quantizes torch's exact bf16 -> fp32 widening of its input."""
+    rng = np.random.default_rng(seed)
+    xt = torch.from_numpy(rng.standard_normal((144, 12)).astype(np.float32)).to(torch.bfloat16)
+    bits = xt.view(torch.int16).numpy().view(np.uint16)
+    got = oracle.train.quantize_per_channel_group_bf16(bits)
+    ref = oracle.train.quantize_per_channel_group(xt.float().numpy())
+    assert np.array_equal(got[0], ref[0]) and np.array_equal(got[1], ref[1])
+
+
+def pin_block_quant_commutes_with_transpose(seed=61):
+    """A 128 x 128 block is square: quantizing W^T block-wise gives W's codes and block scales
+    transposed, partial edge blocks included (N = 200, K = 272)."""
+    rng = np.random.default_rng(seed)
+    w = (rng.standard_normal((200, 272)) * np.exp2(rng.uniform(-4, 4, size=(200, 1)))).astype(np.float32)
+    qt_ref, st_ref = oracle.quant.quantize_per_block(np.ascontiguousarray(w.T))
+    qt, st = oracle.train.transpose_blocks(*oracle.quant.quantize_per_block(w))
+    assert qt.shape == (272, 200) and st.shape == (3, 2)
+    assert np.array_equal(qt, qt_ref) and np.array_equal(st, st_ref)
+
+
+def exact_gemm_row_scaled(qa, sa, qb, sb):
+    """Exact rational D with per-row group scales on both operands (brute force, tiny shapes)."""
+    m, k = qa.shape
+    n = qb.shape[0]
+    out, mag = [[Fraction(0)] * n for _ in range(m)], [[Fraction(0)] * n for _ in range(m)]
+    for i in range(m):
+        for j in range(n):
+            tot = tot_abs = Fraction(0)
+            for kb in range(-(-k // 128)):
+                scale = Fraction(float(sa[i, kb])) * Fraction(float(sb[j, kb]))
+                for kk in range(128 * kb, min(128 * kb + 128, k)):
+                    t = _TABLE[int(qa[i, kk])] * _TABLE[int(qb[j, kk])] * scale
+                    tot += t
+                    tot_abs += abs(t)
+            out[i][j], mag[i][j] = tot, tot_abs
+    return out, mag
+
+
+def pin_row_scaled_gemm_exact(seed=67):
+    """The both-sides row-scaled GEMM against exact rational arithmetic (K ragged, 2.1 groups)."""
+    rng = np.random.default_rng(seed)
+    m, n, k = 3, 5, 272
+    codes = oracle.e4m3.all_finite_codes()
+    qa = rng.choice(codes, size=(m, k)).astype(np.uint8)
+    qb = rng.choice(codes, size=(n, k)).astype(np.uint8)
+    sa = np.exp2(rng.uniform(-8, 2, size=(m, 3))).astype(np.float32)
+    sb = np.exp2(rng.uniform(-12, -2, size=(n, 3))).astype(np.float32)
+    got = oracle.train.gemm_nt_row_scaled(qa, sa, qb, sb)
+    ex, mag = exact_gemm_row_scaled(qa, sa, qb, sb)
+    for i in range(m):
+        for j in range(n):
+            bound = Fraction(k + 1) * Fraction(2) ** -53 * mag[i][j]
+            assert abs(Fraction(float(got[i, j])) - ex[i][j]) <= bound, (i, j)
+
+
+def pin_row_scaled_reduces_to_block_scaled(seed=71):
+    """Per-row scales that are constant over each 128-row block give the block-scaled GEMM."""
+    rng = np.random.default_rng(seed)
+    qa, sa, qb, sb = _random_operands(rng, 4, 200, 384)
+    sb_rows = np.repeat(sb, 128, axis=0)[:200]
+    got = oracle.train.gemm_nt_row_scaled(qa, sa, qb, sb_rows)
+    ref = oracle.gemm.gemm_nt(qa, sa, qb, sb)
+    assert np.array_equal(got, ref)
+
+
+def _exactly_quantizable(rng, rows, cols):
+    """Values whose every 128-group, along rows and along columns (and every 128 x 128 block),
+    contains +-448 and otherwise powers of two in [2^-4, 2^8] or 0: every scale is exactly 1 and
+    every value an exact E4M3 code, so quantization is the identity (and sums stay exact in fp64)."""
+    v = np.exp2(rng.integers(-4, 9, size=(rows, cols))).astype(np.float32)
+    v *= rng.choice(np.array([-1.0, 0.0, 1.0], dtype=np.float32), size=(rows, cols))
+    r, c = np.indices((rows, cols))
+    v[(r % 128) == (c % 128)] = np.float32(448.0)
+    return v
+
+
+def pin_linear_layer_identities(seed=73):
+    """On exactly quantizable operands the forward, dgrad and wgrad compositions must return the
+    exact products X W^T, dY W and dY^T X: a transposed operand or scale, or a wrong grouping,
+    breaks at least one of them."""
+    rng = np.random.default_rng(seed)
+    m, n, k = 256, 384, 256
+    x = _exactly_quantizable(rng, m, k)
+    w = _exactly_quantizable(rng, n, k)
+    dy = _exactly_quantizable(rng, m, n)
+    x64, w64, dy64 = x.astype(np.float64), w.astype(np.float64), dy.astype(np.float64)
+    assert np.array_equal(oracle.train.linear_forward(x, w), x64 @ w64.T)
+    assert np.array_equal(oracle.train.linear_dgrad(dy, w), dy64 @ w64)
+    assert np.array_equal(oracle.train.linear_wgrad(dy, x), dy64.T @ x64)
+
+
 ALL_PINS = [
     pin_e4m3_named_codes, pin_e4m3_decode_vs_torch, pin_e4m3_roundtrip, pin_e4m3_encode_vs_torch,
     pin_e4m3_ties_and_saturation, pin_e4m3_brute_force_sample,
@@ -513,4 +636,7 @@ ALL_PINS = [
     pin_gemm_invariants, pin_gemm_grouped,
     pin_bf16_decode_vs_torch, pin_bf16_named_values, pin_quant_bf16_matches_widened,
     pin_quant_ragged_k, pin_gemm_ragged_k_exact,
+    pin_channel_quant_brute_force, pin_channel_quant_is_token_quant_of_transpose, pin_channel_quant_bf16_widening,
+    pin_block_quant_commutes_with_transpose, pin_row_scaled_gemm_exact, pin_row_scaled_reduces_to_block_scaled,
+    pin_linear_layer_identities,
 ]

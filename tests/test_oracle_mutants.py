@@ -13,6 +13,7 @@ E = oracle.e4m3
 Q = oracle.quant
 G = oracle.gemm
 B = oracle.bf16
+T = oracle.train
 
 _orig_encode = E.encode
 _orig_decode = E.decode
@@ -148,6 +149,38 @@ def _quant_tail_scale_from_full_window(x):
     return q[:, :k], s
 
 
+_orig_channel = T.quantize_per_channel_group
+_orig_wgrad = T.linear_wgrad
+
+def _channel_quant_whole_column(x):
+    """Per-channel quantizer with one scale over the whole column instead of per 128 tokens."""
+    x = np.asarray(x, dtype=np.float32)
+    m, k = x.shape
+    amax = np.max(np.abs(x), axis=0)
+    s = np.where(amax == 0, np.float32(1), amax / np.float32(448)).astype(np.float32)
+    q = E.encode((x / s[None, :]).astype(np.float32)).T.copy()
+    return q, np.repeat(s[:, None], -(-m // 128), axis=1)
+
+
+def _channel_quant_not_transposed(x):
+    """Per-channel scales right, codes left in x's own (M, K) layout read as (K, M)."""
+    qt, st = _orig_channel(x)
+    return qt.T.copy().reshape(qt.shape), st
+
+
+def _transpose_blocks_keeps_scales(q, s):
+    return np.ascontiguousarray(np.asarray(q).T), np.asarray(s)
+
+
+def _row_scaled_uses_block_index(qa, sa, qb, sb):
+    sb_block = np.asarray(sb)[::128]
+    return G.dequantize_rows(qa, sa) @ G.dequantize_rows(qb, np.repeat(sb_block, 128, axis=0)[:qb.shape[0]]).T
+
+
+def _wgrad_swapped(dy, x):
+    return _orig_wgrad(x, dy)
+
+
 _orig_gemm_nt = G.gemm_nt
 _orig_tok = Q.quantize_per_token_group
 
@@ -169,6 +202,11 @@ MUTANTS = {
     "bf16_decode_shift8": (B, "decode", _bf16_decode_shift8),
     "gemm_drops_ragged_k_tail": (G, "gemm_nt", _gemm_drops_k_tail),
     "quant_ragged_tail_wrapped_scale": (Q, "quantize_per_token_group", _quant_tail_scale_from_full_window),
+    "channel_quant_whole_column": (T, "quantize_per_channel_group", _channel_quant_whole_column),
+    "channel_quant_not_transposed": (T, "quantize_per_channel_group", _channel_quant_not_transposed),
+    "transpose_blocks_keeps_scales": (T, "transpose_blocks", _transpose_blocks_keeps_scales),
+    "row_scaled_gemm_block_index": (T, "gemm_nt_row_scaled", _row_scaled_uses_block_index),
+    "wgrad_operands_swapped": (T, "linear_wgrad", _wgrad_swapped),
 }
 
 
