@@ -13,6 +13,10 @@ Functions carry the C names:
 * ``dg_gemm_fp8_nt(a, sa, b, sb)``    -> d bf16 (M, N)
 * ``dg_gemm_fp8_grouped_contiguous(a, sa, b, sb, m_indices)``  -> d bf16 (M_total, N)
 * ``dg_gemm_fp8_grouped_masked(a, sa, b, sb, masked_m)``       -> d bf16 (G, M_max, N)
+* training-side layouts: ``dg_quantize_per_channel_group(x)`` -> (qt uint8 (K, M), st float32
+  (ceil(M/128), ld_st)) in groups of 128 tokens per column, transposed (fp32 or bf16 x);
+  ``dg_transpose_blocks(q, s)`` -> the block quantization of the transposed matrix;
+  ``dg_gemm_fp8_nt_row_scaled(a, sa, b, sb)`` -> d bf16 (M, N) with per-row scales on both operands
 * utilities ``dg_get_num_cus``, ``dg_set_num_cus``,
   ``dg_get_m_alignment_for_contiguous_layout``, ``dg_get_scale_ld``,
   ``dg_gemm_workspace_size``.
@@ -49,6 +53,12 @@ _SIGNATURES = {
                                                       _c_int64, _c_int64, _c_int64, _vp]),
     "dg_gemm_fp8_grouped_masked": (ctypes.c_int, [_vp, _vp, _c_int64, _vp, _vp, _vp, _vp, _c_int64,
                                                   _c_int64, _c_int64, _c_int64, _vp, ctypes.c_size_t, _vp]),
+    "dg_gemm_fp8_nt_row_scaled": (ctypes.c_int, [_vp, _vp, _c_int64, _vp, _vp, _c_int64, _vp, _c_int64, _c_int64,
+                                                 _c_int64, _vp, ctypes.c_size_t, _vp]),
+    "dg_quantize_per_channel_group": (ctypes.c_int, [_vp, _c_int64, _c_int64, _c_int64, _vp, _vp, _c_int64, _vp]),
+    "dg_quantize_per_channel_group_bf16": (ctypes.c_int, [_vp, _c_int64, _c_int64, _c_int64, _vp, _vp, _c_int64,
+                                                          _vp]),
+    "dg_transpose_blocks": (ctypes.c_int, [_vp, _vp, _c_int64, _c_int64, _c_int64, _vp, _vp, _vp]),
     "dg_get_num_cus": (ctypes.c_int, []),
     "dg_set_num_cus": (ctypes.c_int, [ctypes.c_int]),
     "dg_get_m_alignment_for_contiguous_layout": (ctypes.c_int, []),
@@ -140,7 +150,8 @@ def dg_gemm_workspace_size(m, n, k, num_groups=1):
 
 
 def dg_gemm_config_name(layout, m, n, k, num_groups=1):
-    """Tile configuration / K split the GEMM picks (layout 0 normal, 1 contiguous, 2 masked)."""
+    """Tile configuration / K split the GEMM picks (layout 0 normal, 1 contiguous, 2 masked,
+    3 row-scaled normal)."""
     return lib().dg_gemm_config_name(int(layout), int(m), int(n), int(k), int(num_groups)).decode()
 
 
@@ -207,6 +218,50 @@ def dg_quantize_per_block(w, q=None, sb=None):
     return q, sb
 
 
+def dg_quantize_per_channel_group(x, qt=None, st=None):
+    """x float32 or bfloat16 (M, K) -> (qt uint8 (K, M), st float32 (ceil(M/128), ld_st)): groups of 128
+    consecutive tokens of one column, codes transposed (qt[col, tok] encodes x[tok, col]), scales in
+    the activation-scale layout of x^T.  x (G, M, K) -> (qt (G, K, M), st (G, ceil(M/128), ld_st))."""
+    _require(x.dtype in (torch.float32, torch.bfloat16) and x.dim() in (2, 3),
+             "x must be float32 or bfloat16, (M, K) or (G, M, K)")
+    grouped = x.dim() == 3
+    g, m, k = (x.shape if grouped else (1,) + tuple(x.shape))
+    mb = max(-(-m // 128), 1)
+    if qt is None:
+        qt = torch.empty(((g,) if grouped else ()) + (k, m), dtype=torch.uint8, device=x.device)
+    if st is None:
+        st = torch.empty(((g,) if grouped else ()) + (mb, dg_get_scale_ld(k)), dtype=torch.float32, device=x.device)
+    qt = _bytes(qt)
+    _dev(x, qt, st)
+    name = "dg_quantize_per_channel_group" + ("_bf16" if x.dtype == torch.bfloat16 else "")
+    _check(name, getattr(lib(), name)(_ptr(x), g, m, k, _ptr(qt), _ptr(st), st.shape[-1], _stream(x)))
+    return qt, st
+
+
+def dg_quantize_per_channel_group_bf16(x, qt=None, st=None):
+    """bfloat16 x (M, K) or (G, M, K) -> (qt, st): dg_quantize_per_channel_group_bf16."""
+    _require(x.dtype == torch.bfloat16, "x must be bfloat16")
+    return dg_quantize_per_channel_group(x, qt=qt, st=st)
+
+
+def dg_transpose_blocks(q, s, qt=None, st=None):
+    """Block-quantized (q uint8 ([G,] R, C), s ([G,] ceil(R/128), ceil(C/128))) -> the same for the
+    transposed matrix: (qt ([G,] C, R), st ([G,] ceil(C/128), ceil(R/128)))."""
+    q = _bytes(q)
+    _require(q.dim() in (2, 3) and s.dim() == q.dim() and s.dtype == torch.float32, "q (R, C) or (G, R, C), s float32")
+    grouped = q.dim() == 3
+    g, r, c = (q.shape if grouped else (1,) + tuple(q.shape))
+    lead = (g,) if grouped else ()
+    if qt is None:
+        qt = torch.empty(lead + (c, r), dtype=torch.uint8, device=q.device)
+    if st is None:
+        st = torch.empty(lead + (s.shape[-1], s.shape[-2]), dtype=torch.float32, device=q.device)
+    qt = _bytes(qt)
+    _dev(q, s, qt, st)
+    _check("dg_transpose_blocks", lib().dg_transpose_blocks(_ptr(q), _ptr(s), g, r, c, _ptr(qt), _ptr(st), _stream(q)))
+    return qt, st
+
+
 # ---------------------------------------------------------------------------
 # GEMMs
 # ---------------------------------------------------------------------------
@@ -225,6 +280,25 @@ def dg_gemm_fp8_nt(a, sa, b, sb, d=None, workspace=None, use_workspace=True):
     _check("dg_gemm_fp8_nt",
            lib().dg_gemm_fp8_nt(_ptr(a), _ptr(sa), sa.shape[-1], _ptr(b), _ptr(sb), _ptr(d), m, n, k,
                                 _ptr(workspace), ws_bytes, _stream(a)))
+    return d
+
+
+def dg_gemm_fp8_nt_row_scaled(a, sa, b, sb, d=None, workspace=None, use_workspace=True):
+    """D (M, N) bf16 = A (M, K) * B (N, K)^T where both operands carry per-row group scales:
+    sa (ceil(K/128), ld_sa >= M), sb (ceil(K/128), ld_sb >= N) - e.g. the weight gradient
+    dW = dY^T X from dg_quantize_per_channel_group(dY) and dg_quantize_per_channel_group(X)."""
+    a, b = _bytes(a), _bytes(b)
+    m, k = a.shape
+    n = b.shape[0]
+    if d is None:
+        d = torch.empty((m, n), dtype=torch.bfloat16, device=a.device)
+    _dev(a, sa, b, sb, d)
+    if workspace is None and use_workspace:
+        workspace = default_workspace(a.device, dg_gemm_workspace_size(m, n, k, 1))
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check("dg_gemm_fp8_nt_row_scaled",
+           lib().dg_gemm_fp8_nt_row_scaled(_ptr(a), _ptr(sa), sa.shape[-1], _ptr(b), _ptr(sb), sb.shape[-1], _ptr(d),
+                                           m, n, k, _ptr(workspace), ws_bytes, _stream(a)))
     return d
 
 

@@ -20,8 +20,14 @@ int launch_quant_token_group_bf16(const uint16_t* x, int64_t groups, int64_t m, 
                                   int64_t ld_sa, hipStream_t stream);
 int launch_quant_block(const float* w, int64_t groups, int64_t n, int64_t k, uint8_t* q, float* sb,
                        hipStream_t stream);
+int launch_quant_channel_group(const float* x, int64_t mats, int64_t m, int64_t k, uint8_t* qt, float* st,
+                               int64_t ld_st, hipStream_t stream);
+int launch_quant_channel_group_bf16(const uint16_t* x, int64_t mats, int64_t m, int64_t k, uint8_t* qt, float* st,
+                                    int64_t ld_st, hipStream_t stream);
+int launch_transpose_blocks(const uint8_t* q, const float* s, int64_t groups, int64_t r, int64_t c, uint8_t* qt,
+                            float* st, hipStream_t stream);
 int launch_gemm(int layout, const uint8_t* a, const float* sa, int64_t ld_sa, const uint8_t* b,
-                const float* sb, uint16_t* d, const int32_t* m_indices, const int32_t* masked_m,
+                const float* sb, int64_t ld_sb, uint16_t* d, const int32_t* m_indices, const int32_t* masked_m,
                 int64_t groups, int64_t m, int64_t n, int64_t k, void* ws, size_t ws_bytes,
                 hipStream_t stream, int num_cus);
 size_t gemm_workspace_size(int64_t m, int64_t n, int64_t k, int64_t groups, int num_cus);
@@ -170,7 +176,7 @@ int dg_gemm_fp8_nt(const uint8_t* a, const float* sa, int64_t ld_sa, const uint8
   DG_REQUIRE(workspace == nullptr || aligned16(workspace), "gemm: workspace must be 16-byte aligned");
   const int cus = effective_cus();
   if (cus < 0) return cus;
-  return launch_gemm(0, a, sa, ld_sa, b, sb, d, nullptr, nullptr, 1, m, n, k, workspace,
+  return launch_gemm(0, a, sa, ld_sa, b, sb, 0, d, nullptr, nullptr, 1, m, n, k, workspace,
                      workspace ? workspace_bytes : 0, static_cast<hipStream_t>(stream), cus);
 }
 
@@ -186,7 +192,7 @@ int dg_gemm_fp8_grouped_contiguous(const uint8_t* a, const float* sa, int64_t ld
   DG_REQUIRE(m_indices != nullptr, "contiguous gemm: m_indices is null");
   const int cus = effective_cus();
   if (cus < 0) return cus;
-  return launch_gemm(1, a, sa, ld_sa, b, sb, d, m_indices, nullptr, num_groups, m_total, n, k,
+  return launch_gemm(1, a, sa, ld_sa, b, sb, 0, d, m_indices, nullptr, num_groups, m_total, n, k,
                      nullptr, 0, static_cast<hipStream_t>(stream), cus);
 }
 
@@ -204,14 +210,67 @@ int dg_gemm_fp8_grouped_masked(const uint8_t* a, const float* sa, int64_t ld_sa,
   DG_REQUIRE(workspace == nullptr || aligned16(workspace), "gemm: workspace must be 16-byte aligned");
   const int cus = effective_cus();
   if (cus < 0) return cus;
-  return launch_gemm(2, a, sa, ld_sa, b, sb, d, nullptr, masked_m, num_groups, m_max, n, k,
+  return launch_gemm(2, a, sa, ld_sa, b, sb, 0, d, nullptr, masked_m, num_groups, m_max, n, k,
                      workspace, workspace ? workspace_bytes : 0, static_cast<hipStream_t>(stream), cus);
+}
+
+int dg_gemm_fp8_nt_row_scaled(const uint8_t* a, const float* sa, int64_t ld_sa, const uint8_t* b,
+                              const float* sb, int64_t ld_sb, uint16_t* d, int64_t m, int64_t n, int64_t k,
+                              void* workspace, size_t workspace_bytes, dg_stream_t stream) {
+  const int c = check_gemm_common(a, sa, ld_sa, b, sb, d, m, n, k);
+  if (c <= 0) return c;
+  DG_REQUIRE(ld_sb >= n && ld_sb % 4 == 0, "row-scaled gemm: need ld_sb >= n and ld_sb %% 4 == 0 (ld_sb=%lld n=%lld)",
+             (long long)ld_sb, (long long)n);
+  DG_REQUIRE(workspace == nullptr || aligned16(workspace), "gemm: workspace must be 16-byte aligned");
+  const int cus = effective_cus();
+  if (cus < 0) return cus;
+  return launch_gemm(3, a, sa, ld_sa, b, sb, ld_sb, d, nullptr, nullptr, 1, m, n, k, workspace,
+                     workspace ? workspace_bytes : 0, static_cast<hipStream_t>(stream), cus);
+}
+
+static int check_channel_group(const void* x, int64_t num_groups, int64_t m, int64_t k, uint8_t* qt, float* st,
+                               int64_t ld_st) {
+  DG_REQUIRE(num_groups >= 0 && m >= 0 && m % kKAlign == 0 && k >= 0 && k % 4 == 0,
+             "quantize_per_channel_group: need groups >= 0, m >= 0, m %% 16 == 0, k >= 0, k %% 4 == 0 "
+             "(m=%lld k=%lld)", (long long)m, (long long)k);
+  DG_REQUIRE(ld_st >= k && ld_st % 4 == 0, "quantize_per_channel_group: need ld_st >= k and ld_st %% 4 == 0 (ld_st=%lld)",
+             (long long)ld_st);
+  if (m == 0 || k == 0 || num_groups == 0) return DG_OK;
+  DG_REQUIRE(x && qt && st, "quantize_per_channel_group: null pointer");
+  DG_REQUIRE(aligned16(x) && aligned16(qt) && aligned16(st), "quantize_per_channel_group: pointers must be 16-byte aligned");
+  return 1;   // proceed
+}
+
+int dg_quantize_per_channel_group(const float* x, int64_t num_groups, int64_t m, int64_t k, uint8_t* qt, float* st,
+                                  int64_t ld_st, dg_stream_t stream) {
+  const int c = check_channel_group(x, num_groups, m, k, qt, st, ld_st);
+  if (c <= 0) return c;
+  return launch_quant_channel_group(x, num_groups, m, k, qt, st, ld_st, static_cast<hipStream_t>(stream));
+}
+
+int dg_quantize_per_channel_group_bf16(const uint16_t* x, int64_t num_groups, int64_t m, int64_t k, uint8_t* qt,
+                                       float* st, int64_t ld_st, dg_stream_t stream) {
+  const int c = check_channel_group(x, num_groups, m, k, qt, st, ld_st);
+  if (c <= 0) return c;
+  return launch_quant_channel_group_bf16(x, num_groups, m, k, qt, st, ld_st, static_cast<hipStream_t>(stream));
+}
+
+int dg_transpose_blocks(const uint8_t* q, const float* s, int64_t num_groups, int64_t rows, int64_t cols, uint8_t* qt,
+                        float* st, dg_stream_t stream) {
+  DG_REQUIRE(num_groups >= 0 && rows >= 0 && cols >= 0 && rows % kKAlign == 0 && cols % kKAlign == 0,
+             "transpose_blocks: need groups >= 0 and rows, cols >= 0 multiples of 16 (rows=%lld cols=%lld)",
+             (long long)rows, (long long)cols);
+  if (num_groups == 0 || rows == 0 || cols == 0) return DG_OK;
+  DG_REQUIRE(q && s && qt && st, "transpose_blocks: null pointer");
+  DG_REQUIRE(aligned16(q) && aligned16(qt), "transpose_blocks: code pointers must be 16-byte aligned");
+  DG_REQUIRE(q != qt, "transpose_blocks: in-place transpose is not supported");
+  return launch_transpose_blocks(q, s, num_groups, rows, cols, qt, st, static_cast<hipStream_t>(stream));
 }
 
 const char* dg_gemm_config_name(int layout, int64_t m, int64_t n, int64_t k, int64_t num_groups) {
   static thread_local char buf[96];
   buf[0] = 0;
-  if (layout < 0 || layout > 2 || m <= 0 || n <= 0 || k <= 0 || k % kKAlign || num_groups <= 0) return buf;
+  if (layout < 0 || layout > 3 || m <= 0 || n <= 0 || k <= 0 || k % kKAlign || num_groups <= 0) return buf;
   const int cus = effective_cus();
   if (cus < 0) return buf;
   gemm_config_name(layout, m, n, k, num_groups, cus, buf, sizeof(buf));

@@ -70,6 +70,8 @@ struct Cfg {
   static constexpr int kSbCount = (BN + 127) / 128;             // 128-row weight blocks of a tile
   static constexpr int kSbWaveBytes = 16 * ((kSbCount * 4 + 15) / 16);   // one copy per wave
   static constexpr int kStageBytes = kSbOffset + kWaves * kSbWaveBytes;
+  // per-row B scales (kDenseRowB): BN floats = BN/4 16-byte chunks, spread over the waves' lanes
+  static constexpr int kSbRowLanesPerWave = (BN / 4 + kWaves - 1) / kWaves;
   static constexpr int kDmaRows = 8;                          // one DMA instruction = 8 rows x 128 B
   static constexpr int kDmaB = BN / kDmaRows;                 // DMA instructions per stage, weights
   static constexpr int kDma = (BN + BM) / kDmaRows;           // ... weights + activations
@@ -83,7 +85,15 @@ struct Cfg {
   static_assert(STAGES >= 2 && STAGES <= 4, "2..4 stages");
   static_assert(kVmPerStage * (STAGES - 1) < 64, "vmcnt range");
   static_assert(kSaLanesPerWave <= 64 && BM % 4 == 0, "scale DMA shape");
+  static_assert(kSbRowLanesPerWave <= 64 && BN % 4 == 0, "row-scale DMA shape");
 };
+
+// Bytes of one LDS stage: the operand tiles, the activation scales, then the B scales (per-wave
+// copies of the tile's block scales, or BN per-row scales for kDenseRowB).
+template <class C, int LAYOUT>
+constexpr int stage_bytes() {
+  return C::kSbOffset + (LAYOUT == kDenseRowB ? C::BN * 4 : C::kWaves * C::kSbWaveBytes);
+}
 
 // LDS slot of 16-byte chunk c of tile row r.  f depends on r mod 16 only, so every fragment
 // of a lane shares one pattern and fragment addresses differ by immediates.
@@ -123,10 +133,12 @@ template <class C, int LAYOUT>
 __global__ __launch_bounds__(C::kThreads) void gemm_fp8_kernel(GemmParams p) {
   constexpr int NT = C::kThreads;
   constexpr int S = C::STAGES;
-  __shared__ __attribute__((aligned(1024))) uint8_t st0[C::kStageBytes];
-  __shared__ __attribute__((aligned(1024))) uint8_t st1[C::kStageBytes];
-  __shared__ __attribute__((aligned(1024))) uint8_t st2[S > 2 ? C::kStageBytes : 16];
-  __shared__ __attribute__((aligned(1024))) uint8_t st3[S > 3 ? C::kStageBytes : 16];
+  constexpr bool kRowB = LAYOUT == kDenseRowB;
+  constexpr int kStage = stage_bytes<C, LAYOUT>();
+  __shared__ __attribute__((aligned(1024))) uint8_t st0[kStage];
+  __shared__ __attribute__((aligned(1024))) uint8_t st1[kStage];
+  __shared__ __attribute__((aligned(1024))) uint8_t st2[S > 2 ? kStage : 16];
+  __shared__ __attribute__((aligned(1024))) uint8_t st3[S > 3 ? kStage : 16];
   __shared__ int s_prefix[LAYOUT == kMasked ? 1025 : 1];
   __shared__ int s_scan[LAYOUT == kMasked ? 256 : 1];
   __shared__ int s_flag;
@@ -230,15 +242,21 @@ __global__ __launch_bounds__(C::kThreads) void gemm_fp8_kernel(GemmParams p) {
     int sa_src_row = m0 + 4 * sa_lane;
     sa_src_row = sa_src_row + 4 <= p.ld_sa ? sa_src_row : (int)p.ld_sa - 4;
     const uint32_t sa_src = (uint32_t)sa_src_row * 4u;   // byte offset within the kb row
-    // weight scales: lane i < kSbCount of every wave fetches the scale of weight block n0/128 + i
-    // into the wave's own copy (keeps the per-wave vmcnt accounting uniform)
-    const bool sb_active = lane < C::kSbCount;
+    // B scales.  Block scales: lane i < kSbCount of every wave fetches the scale of weight block
+    // n0/128 + i into the wave's own copy (keeps the per-wave vmcnt accounting uniform).  Per-row
+    // scales (kDenseRowB): as the activation scales, lanes of every wave fetch the BN/4 16-byte
+    // chunks of sb[kb][n0 .. n0+BN), clamped to the caller's ld_sb row.
+    const int sbr_lane = wave * C::kSbRowLanesPerWave + lane;
+    const bool sb_active = kRowB ? (lane < C::kSbRowLanesPerWave && sbr_lane < C::BN / 4) : lane < C::kSbCount;
     int sb_blk = (n0 >> 7) + lane;
     sb_blk = sb_blk < p.nb128 ? sb_blk : p.nb128 - 1;
-    const uint32_t sb_src = (uint32_t)sb_blk * (uint32_t)p.kb_total * 4u;
+    int sbr_row = n0 + 4 * sbr_lane;
+    sbr_row = sbr_row + 4 <= p.ld_sb ? sbr_row : (int)p.ld_sb - 4;
+    const uint32_t sb_src = kRowB ? (uint32_t)sbr_row * 4u : (uint32_t)sb_blk * (uint32_t)p.kb_total * 4u;
     const int sb_idx = ((n0 + wn0) >> 7) - (n0 >> 7);   // this wave's block within the tile
     const __amdgpu_buffer_rsrc_t rs_sa = make_rsrc(sa_g, (int64_t)p.kb_total * p.ld_sa * 4);
-    const __amdgpu_buffer_rsrc_t rs_sb = make_rsrc(sb_g, (int64_t)p.nb128 * p.kb_total * 4);
+    const __amdgpu_buffer_rsrc_t rs_sb =
+        make_rsrc(sb_g, kRowB ? (int64_t)p.kb_total * p.ld_sb * 4 : (int64_t)p.nb128 * p.kb_total * 4);
 
     v4f acc[C::kFragN][C::kFragM];
 #pragma unroll
@@ -271,8 +289,12 @@ __global__ __launch_bounds__(C::kThreads) void gemm_fp8_kernel(GemmParams p) {
       }
       if (sa_active)
         lds_dma16(rs_sa, sbase + C::kSaOffset + 16 * wave * C::kSaLanesPerWave, sa_src, kb * (int)p.ld_sa * 4);
-      if (sb_active)
-        lds_dma4(rs_sb, sbase + C::kSbOffset + wave * C::kSbWaveBytes, sb_src, kb * 4);
+      if (sb_active) {
+        if constexpr (kRowB)
+          lds_dma16(rs_sb, sbase + C::kSbOffset + 16 * wave * C::kSbRowLanesPerWave, sb_src, kb * (int)p.ld_sb * 4);
+        else
+          lds_dma4(rs_sb, sbase + C::kSbOffset + wave * C::kSbWaveBytes, sb_src, kb * 4);
+      }
     };
     auto issue_rt = [&](int tk, int slot) {
       if (slot == 0) issue(tk, IC<0>{});
@@ -306,10 +328,21 @@ __global__ __launch_bounds__(C::kThreads) void gemm_fp8_kernel(GemmParams p) {
                           *reinterpret_cast<const u32x4*>(sbase + (off ^ 16)));
       }
       const float* sa_l = reinterpret_cast<const float*>(sbase + C::kSaOffset);
-      const float sbv = sa_l[C::BM + wave * (C::kSbWaveBytes / 4) + sb_idx];   // this wave's copy
+      // block scales: scale[j] = fl32(sa * sb) of the lane's row, the wave's weight block; per-row
+      // B scales: scale[j] = sa, and the 4 scales of the lane's 4 B rows of fragment i in sbr[i]
       float scale[C::kFragM];
+      v4f sbr[kRowB ? C::kFragN : 1];
+      if constexpr (kRowB) {
 #pragma unroll
-      for (int j = 0; j < C::kFragM; ++j) scale[j] = sa_l[wm0 + 16 * j + l16] * sbv;   // fl32(sa * sb)
+        for (int j = 0; j < C::kFragM; ++j) scale[j] = sa_l[wm0 + 16 * j + l16];
+#pragma unroll
+        for (int i = 0; i < C::kFragN; ++i)
+          sbr[i] = *reinterpret_cast<const v4f*>(sbase + C::kSbOffset + 4 * (wn0 + 16 * i + 4 * g4));
+      } else {
+        const float sbv = sa_l[C::BM + wave * (C::kSbWaveBytes / 4) + sb_idx];   // this wave's copy
+#pragma unroll
+        for (int j = 0; j < C::kFragM; ++j) scale[j] = sa_l[wm0 + 16 * j + l16] * sbv;   // fl32(sa * sb)
+      }
 
       constexpr int Q = C::kFragN * C::kFragM;
       v8i aop[2];
@@ -330,7 +363,8 @@ __global__ __launch_bounds__(C::kThreads) void gemm_fp8_kernel(GemmParams p) {
           const int i = (q - 1) / C::kFragM, j = (q - 1) % C::kFragM;
 #pragma unroll
           for (int r = 0; r < 4; ++r)
-            acc[i][j][r] = __builtin_fmaf(part[(q - 1) & 1][r], scale[j], acc[i][j][r]);
+            acc[i][j][r] = __builtin_fmaf(part[(q - 1) & 1][r], kRowB ? scale[j] * sbr[kRowB ? i : 0][r] : scale[j],
+                                          acc[i][j][r]);   // kRowB: fl32(sa * sb) per element
         }
         if (q > 0 && q < Q) {
           __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA of q
@@ -479,7 +513,11 @@ using CfgDec128 = Cfg<64, 128, 32, 64, 3>;
 template <int LAYOUT>
 static LaunchInfo cfg_info(int cfg) {
   switch (cfg) {
-    case kCfgWide: return info<CfgWide, LAYOUT>();
+    // per-row B scales hold one float4 per weight fragment row: the 256x192 tile's registers
+    // have no room for them, so kDenseRowB runs its large shapes on 256x128
+    case kCfgWide:
+      if constexpr (LAYOUT == kDenseRowB) return info<CfgLarge, LAYOUT>();
+      else return info<CfgWide, LAYOUT>();
     case kCfgDec64: return info<CfgDec64, LAYOUT>();
     case kCfgDec128: return info<CfgDec128, LAYOUT>();
     case kCfgRows128: return info<CfgRows128, LAYOUT>();
@@ -587,7 +625,7 @@ static Plan make_decode_plan(int64_t m, int64_t n, int64_t k, int64_t groups, in
 static Plan make_plan(int layout, int64_t m, int64_t n, int64_t k, int64_t groups, int num_cus, bool allow_split) {
   if (layout != kContiguous && m <= 128) return make_decode_plan(m, n, k, groups, num_cus, allow_split);
   Plan pl{};
-  pl.cfg = layout == kContiguous ? kCfgRows128 : choose_large(m, n, groups, num_cus);
+  pl.cfg = layout == kContiguous ? kCfgRows128 : layout == kDenseRowB ? kCfgLarge : choose_large(m, n, groups, num_cus);
   const LaunchInfo li = cfg_info<kDense>(pl.cfg);
   const int kb_total = (int)((k + kGroup - 1) / kGroup);
   pl.splits = 1;
@@ -614,8 +652,11 @@ void gemm_config_name(int layout, int64_t m, int64_t n, int64_t k, int64_t group
 }
 
 size_t gemm_workspace_size(int64_t m, int64_t n, int64_t k, int64_t groups, int num_cus) {
-  const int layout = groups > 1 ? kMasked : kDense;
-  return make_plan(layout, m, n, k, groups, num_cus, true).ws_bytes;
+  if (groups > 1) return make_plan(kMasked, m, n, k, groups, num_cus, true).ws_bytes;
+  // one group: enough for the dense plan and for the per-row-B-scale plan of the same shape
+  const size_t dense = make_plan(kDense, m, n, k, 1, num_cus, true).ws_bytes;
+  const size_t rowb = make_plan(kDenseRowB, m, n, k, 1, num_cus, true).ws_bytes;
+  return dense > rowb ? dense : rowb;
 }
 
 template <int LAYOUT>
@@ -633,7 +674,7 @@ static int launch_layout(GemmParams p, const Plan& pl, hipStream_t stream, int n
 }
 
 int launch_gemm(int layout, const uint8_t* a, const float* sa, int64_t ld_sa, const uint8_t* b,
-                const float* sb, uint16_t* d, const int32_t* m_indices, const int32_t* masked_m,
+                const float* sb, int64_t ld_sb, uint16_t* d, const int32_t* m_indices, const int32_t* masked_m,
                 int64_t groups, int64_t m, int64_t n, int64_t k, void* ws, size_t ws_bytes,
                 hipStream_t stream, int num_cus) {
   if (n * k > 0x7fffffffLL || m * k > 0x7fffffffLL)
@@ -649,8 +690,9 @@ int launch_gemm(int layout, const uint8_t* a, const float* sa, int64_t ld_sa, co
   p.a = a; p.sa = sa; p.b = b; p.sb = sb; p.d = d;
   p.m_indices = m_indices; p.masked_m = masked_m;
   p.ld_sa = ld_sa;
+  p.ld_sb = ld_sb;
   p.m = (int)m; p.n = (int)n; p.k = (int)k;
-  p.num_groups = (int)(layout == kDense ? 1 : groups);
+  p.num_groups = (int)(layout == kDense || layout == kDenseRowB ? 1 : groups);
   p.kb_total = (int)((k + kGroup - 1) / kGroup);
   p.nb128 = (int)((n + kGroup - 1) / kGroup);
   p.tiles_m = pl.tiles_m; p.tiles_n = pl.tiles_n;
@@ -667,6 +709,7 @@ int launch_gemm(int layout, const uint8_t* a, const float* sa, int64_t ld_sa, co
   switch (layout) {
     case kContiguous: return launch_layout<kContiguous>(p, pl, stream, num_cus);
     case kMasked: return launch_layout<kMasked>(p, pl, stream, num_cus);
+    case kDenseRowB: return launch_layout<kDenseRowB>(p, pl, stream, num_cus);
     default: return launch_layout<kDense>(p, pl, stream, num_cus);
   }
 }

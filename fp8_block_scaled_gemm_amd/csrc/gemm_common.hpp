@@ -5,7 +5,10 @@
 
 namespace dg {
 
-enum Layout : int { kDense = 0, kContiguous = 1, kMasked = 2 };
+// kDenseRowB: the dense form whose B operand carries one scale per row per 128-wide K group,
+// in the activation-scale layout sb[kb * ld_sb + row] (both operands per-row: the weight-gradient
+// GEMM of a linear layer), instead of one per 128 x 128 block.
+enum Layout : int { kDense = 0, kContiguous = 1, kMasked = 2, kDenseRowB = 3 };
 
 // Kernel arguments (one struct, passed by value).  Sizes are per group; the
 // strides step from one group's operand to the next (masked layout, weights of
@@ -21,6 +24,7 @@ struct GemmParams {
   float* ws;                  // split-K partials
   unsigned* counters;         // split-K arrival counters, one per output tile
   int64_t ld_sa;
+  int64_t ld_sb;             // kDenseRowB: row stride of the per-row B scales
   int64_t a_gstride, sa_gstride, b_gstride, sb_gstride, d_gstride;   // per-group strides (elements)
   int m;            // rows per group (dense: M, contiguous: M_total, masked: M_max)
   int n, k;

@@ -175,6 +175,63 @@ int dg_gemm_fp8_grouped_masked(const uint8_t* a, const float* sa, int64_t ld_sa,
                                dg_stream_t stream);
 
 /*
+ * Training-side layouts: the backward GEMMs of a linear layer Y = X * W^T.  The pages say the
+ * library serves DeepSeek-V3/R1 training as well as inference (机器之心 report, opening section;
+ * 3loumao explainer, section 03; ai.abqq.net summary, section 3 "application scenarios") but
+ * describe no backward pass.  These entry points keep the fine-grained recipe with the scale
+ * groups along each backward GEMM's own contraction dimension:
+ *   dgrad  dX = dY * W       = dg_gemm_fp8_nt(dY per-token groups, W^T blocks)
+ *          (W^T's 128 x 128 block quantization is W's transposed: dg_transpose_blocks);
+ *   wgrad  dW = dY^T * X     = dg_gemm_fp8_nt_row_scaled(dY^T, X^T), both operands in
+ *          groups of 128 tokens per column (dg_quantize_per_channel_group).
+ */
+
+/*
+ * Per-channel-group quantizer (128 x 1: 128 consecutive tokens of one column), transposed
+ * output, for num_groups stacked (m, k) matrices.  Same rule as the per-token quantizer with
+ * the amax over x[128mb .. 128mb+127, col] (a last group of m % 128 tokens takes its amax over
+ * the tokens present).
+ * x  : fp32 (num_groups, m, k) row-major, read only.
+ * qt : E4M3 bytes (num_groups, k, m) row-major, written: qt[g, col, tok] encodes x[g, tok, col].
+ * st : fp32 scales in the activation-scale layout of the transposed matrix: written at
+ *      st[(g * MB + mb) * ld_st + col] for col < k, MB = ceil(m / 128); other entries untouched.
+ * Errors: DG_ERR_INVALID_ARG for null/misaligned pointers, negative sizes, m % 16 != 0,
+ * k % 4 != 0, ld_st < k or ld_st % 4 != 0.  Output is bit-exact.
+ */
+int dg_quantize_per_channel_group(const float* x, int64_t num_groups, int64_t m, int64_t k, uint8_t* qt, float* st,
+                                  int64_t ld_st, dg_stream_t stream);
+
+/* The per-channel-group quantizer for bf16 input (exact widening, as
+ * dg_quantize_per_token_group_bf16).  Same layouts, errors and guarantees. */
+int dg_quantize_per_channel_group_bf16(const uint16_t* x, int64_t num_groups, int64_t m, int64_t k, uint8_t* qt,
+                                       float* st, int64_t ld_st, dg_stream_t stream);
+
+/*
+ * Transpose of block-quantized matrices: codes q (num_groups, rows, cols) -> qt (num_groups,
+ * cols, rows), block scales s (num_groups, ceil(rows/128), ceil(cols/128)) -> st (num_groups,
+ * ceil(cols/128), ceil(rows/128)).  A 128 x 128 block is square, so (qt, st) is exactly what
+ * dg_quantize_per_block gives for the transposed matrix: the weight operand of the dgrad GEMM.
+ * Errors: DG_ERR_INVALID_ARG for null/misaligned code pointers, negative sizes, rows or cols not
+ * a multiple of 16, q == qt (no in-place transpose).  Bit-exact.
+ */
+int dg_transpose_blocks(const uint8_t* q, const float* s, int64_t num_groups, int64_t rows, int64_t cols, uint8_t* qt,
+                        float* st, dg_stream_t stream);
+
+/*
+ * FP8 GEMM D = A * B^T where both operands carry per-row group scales (the weight-gradient
+ * GEMM): after every 128-deep K block, acc += P * fl32(sa[row, kb] * sb[col, kb]);
+ * D = bf16_rne(acc).
+ * a  : E4M3 (m, k) row-major.   sa : fp32, sa[kb * ld_sa + row], ld_sa >= m.
+ * b  : E4M3 (n, k) row-major.   sb : fp32, sb[kb * ld_sb + col], ld_sb >= n.
+ * d  : bf16 (m, n) row-major, written.
+ * workspace : as dg_gemm_fp8_nt (dg_gemm_workspace_size covers this form too).
+ * Errors: as dg_gemm_fp8_nt, plus ld_sb < n or ld_sb % 4 != 0.  Deterministic.
+ */
+int dg_gemm_fp8_nt_row_scaled(const uint8_t* a, const float* sa, int64_t ld_sa, const uint8_t* b,
+                              const float* sb, int64_t ld_sb, uint16_t* d, int64_t m, int64_t n, int64_t k,
+                              void* workspace, size_t workspace_bytes, dg_stream_t stream);
+
+/*
  * Utilities (CSDN article, "utilities": cap on the compute units used,
  * contiguous-layout alignment, aligned column-major scale tensor).
  */
@@ -194,15 +251,15 @@ int dg_get_m_alignment_for_contiguous_layout(void);
 /* Smallest valid ld_sa for `rows` rows: rows rounded up to a multiple of 4 (16 bytes). */
 int64_t dg_get_scale_ld(int64_t rows);
 
-/* Workspace bytes that let dg_gemm_fp8_nt / dg_gemm_fp8_grouped_masked use
- * split-K for the given shape (m = rows per group; num_groups = 1 for the
+/* Workspace bytes that let dg_gemm_fp8_nt / dg_gemm_fp8_nt_row_scaled /
+ * dg_gemm_fp8_grouped_masked use split-K for the given shape (m = rows per group; num_groups = 1 for the
  * normal GEMM).  0 means split-K is never used for that shape. */
 size_t dg_gemm_workspace_size(int64_t m, int64_t n, int64_t k, int64_t num_groups);
 
 /* Name of the tile configuration and K split the GEMM picks for a shape, as
  * "BNxBM/WNxWM/splitS" (static thread-local string), assuming a large enough
  * workspace.  layout: 0 normal, 1 contiguous-grouped, 2 masked-grouped (m = rows
- * per group).  For profiling and reports; returns "" for invalid arguments. */
+ * per group), 3 row-scaled normal.  For profiling and reports; returns "" for invalid arguments. */
 const char* dg_gemm_config_name(int layout, int64_t m, int64_t n, int64_t k, int64_t num_groups);
 
 #ifdef __cplusplus

@@ -103,3 +103,30 @@ def test_argument_validation(lib):
                                           None) == DG_ERR_INVALID_ARG
     assert lib.dg_gemm_fp8_grouped_masked(fake, fake, 200, fake, fake, fake, fake, 4, 256, 8, 128, None, 0,
                                           None) == DG_ERR_INVALID_ARG     # ld_sa < m_max
+
+
+def test_training_layout_argument_validation(lib):
+    fake, fake2 = _p(0x1000), _p(0x2000)   # aligned, never dereferenced: validation fails first
+    mis = _p(0x1004)
+    for fn in (lib.dg_quantize_per_channel_group, lib.dg_quantize_per_channel_group_bf16):
+        assert fn(fake, 1, 100, 8, fake, fake, 8, None) == DG_ERR_INVALID_ARG    # m % 16 != 0
+        assert fn(fake, 1, 128, 6, fake, fake, 8, None) == DG_ERR_INVALID_ARG    # k % 4 != 0
+        assert fn(fake, 1, 128, 8, fake, fake, 4, None) == DG_ERR_INVALID_ARG    # ld_st < k
+        assert fn(fake, 1, 128, 8, fake, fake, 10, None) == DG_ERR_INVALID_ARG   # ld_st % 4 != 0
+        assert fn(None, 1, 128, 8, fake, fake, 8, None) == DG_ERR_INVALID_ARG
+        assert fn(mis, 1, 128, 8, fake, fake, 8, None) == DG_ERR_INVALID_ARG
+        assert fn(None, 1, 0, 8, None, None, 8, None) == DG_OK                   # empty: no-op
+        assert fn(None, 0, 128, 8, None, None, 8, None) == DG_OK
+    assert lib.dg_transpose_blocks(fake, fake, 1, 100, 128, fake2, fake, None) == DG_ERR_INVALID_ARG   # rows % 16
+    assert lib.dg_transpose_blocks(fake, fake, 1, 128, 120, fake2, fake, None) == DG_ERR_INVALID_ARG   # cols % 16
+    assert lib.dg_transpose_blocks(fake, fake, 1, 128, 128, fake, fake, None) == DG_ERR_INVALID_ARG    # in place
+    assert lib.dg_transpose_blocks(mis, fake, 1, 128, 128, fake2, fake, None) == DG_ERR_INVALID_ARG
+    assert lib.dg_transpose_blocks(None, fake, 1, 128, 128, fake2, fake, None) == DG_ERR_INVALID_ARG
+    assert lib.dg_transpose_blocks(None, None, 1, 0, 128, None, None, None) == DG_OK
+    rs = lambda m, n, k, ld_sa, ld_sb, a=fake: (a, fake, ld_sa, fake, fake, ld_sb, fake, m, n, k, None, 0, None)
+    assert lib.dg_gemm_fp8_nt_row_scaled(*rs(4, 8, 128, 4, 4)) == DG_ERR_INVALID_ARG     # ld_sb < n
+    assert lib.dg_gemm_fp8_nt_row_scaled(*rs(4, 8, 128, 4, 10)) == DG_ERR_INVALID_ARG    # ld_sb % 4 != 0
+    assert lib.dg_gemm_fp8_nt_row_scaled(*rs(4, 8, 100, 4, 8)) == DG_ERR_INVALID_ARG     # k % 16 != 0
+    assert lib.dg_gemm_fp8_nt_row_scaled(*rs(8, 8, 128, 4, 8)) == DG_ERR_INVALID_ARG     # ld_sa < m
+    assert lib.dg_gemm_fp8_nt_row_scaled(*rs(4, 8, 128, 4, 8, a=None)) == DG_ERR_INVALID_ARG
+    assert lib.dg_gemm_fp8_nt_row_scaled(*rs(0, 8, 128, 0, 8, a=None)) == DG_OK           # empty: no-op
