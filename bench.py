@@ -1,7 +1,7 @@
 """Benchmark of the FP8 block-scaled GEMM hot path on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload dense_v3|small|contiguous|masked|
-                     large_dense|zipf] [--no-cpu-baseline] [--cpu-seconds S] [--eager]
+                     large_dense|zipf|train_v3|overlap] [--no-cpu-baseline] [--cpu-seconds S] [--eager]
     python bench.py --copy-calibration      # counter calibration: one plain 1 GiB device copy
 
 One step is one pass of the whole hot path over one batch of synthetic input:
@@ -22,6 +22,10 @@ per-shape GEMM TFLOP/s and HBM GB/s, the roofline of the dominant GEMM kernel
 (with the HBM traffic that rocprofv3 counters measured for it, when the committed
 counter summary matches the kernel source) and the CPU oracle's throughput on a
 bounded sample of the same workload.
+
+The train_v3 workload is a linear layer's training step per DeepSeek-V3 (N, K) at 4096 tokens:
+forward, dgrad (dY W through the transposed weight blocks) and wgrad (dY^T X from per-channel
+token groups, the row-scaled GEMM), with every quantizer and the transpose inside the step.
 
 Workloads: DeepSeek-V3/R1 inference shapes (prefill and decode, no tensor
 parallelism - the pages' own benchmark set, 机器之心 DeepGEMM report,
@@ -51,7 +55,8 @@ def parse():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="dense_v3",
-                    choices=["dense_v3", "small", "contiguous", "masked", "large_dense", "zipf", "overlap"])
+                    choices=["dense_v3", "small", "contiguous", "masked", "large_dense", "zipf", "train_v3",
+                             "overlap"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target CPU work of the oracle sample")
     ap.add_argument("--eager", action="store_true", help="time eager launches instead of graph replays")
@@ -129,6 +134,69 @@ def build_dense(torch, dg, dev, shapes, name, act_dtype="fp32"):
                                                                                          workspace=ws)),
                       flops=2.0 * m * n * k, nbytes=dense_gemm_bytes(m, n, k),
                       config=dg.dg_gemm_config_name(0, m, n, k, 1)))
+    return ops
+
+
+def rowscaled_gemm_bytes(m, n, k):
+    """Algorithmic HBM bytes of one row-scaled GEMM: A + per-row scales, B + per-row scales, bf16 D."""
+    kb = -(-k // 128)
+    return m * k + 4 * m * kb + n * k + 4 * n * kb + 2 * m * n
+
+
+def build_train(torch, dg, dev, m, nk_list):
+    """A linear layer's training step per (N, K) at m tokens: forward Y = X W^T, dgrad dX = dY W (dY in
+    per-token groups, W^T from W's transposed blocks), wgrad dW = dY^T X (both in per-channel token
+    groups, row-scaled GEMM).  Every quantizer and the block transpose run inside the step."""
+    gen = Gen(torch, dev, 4321)
+    ops = []
+    u8, f32 = torch.uint8, torch.float32
+    for (n, k) in nk_list:
+        w32 = gen.normal((n, k), 0.02)
+        x32 = gen.activations(m, k)
+        dy32 = gen.normal((m, n), 1e-2)
+        qw = torch.empty((n, k), dtype=u8, device=dev)
+        sw = torch.empty((-(-n // 128), -(-k // 128)), dtype=f32, device=dev)
+        qwt = torch.empty((k, n), dtype=u8, device=dev)
+        swt = torch.empty((-(-k // 128), -(-n // 128)), dtype=f32, device=dev)
+        qx = torch.empty((m, k), dtype=u8, device=dev)
+        sx = torch.empty((-(-k // 128), dg.dg_get_scale_ld(m)), dtype=f32, device=dev)
+        qdy = torch.empty((m, n), dtype=u8, device=dev)
+        sdy = torch.empty((-(-n // 128), dg.dg_get_scale_ld(m)), dtype=f32, device=dev)
+        qdyt = torch.empty((n, m), dtype=u8, device=dev)
+        sdyt = torch.empty((-(-m // 128), dg.dg_get_scale_ld(n)), dtype=f32, device=dev)
+        qxt = torch.empty((k, m), dtype=u8, device=dev)
+        sxt = torch.empty((-(-m // 128), dg.dg_get_scale_ld(k)), dtype=f32, device=dev)
+        y = torch.empty((m, n), dtype=torch.bfloat16, device=dev)
+        dx = torch.empty((m, k), dtype=torch.bfloat16, device=dev)
+        dw = torch.empty((n, k), dtype=torch.bfloat16, device=dev)
+        ws = dg.default_workspace(dev, max(dg.dg_gemm_workspace_size(m, n, k, 1), dg.dg_gemm_workspace_size(m, k, n, 1),
+                                           dg.dg_gemm_workspace_size(n, k, m, 1)))
+        ops.append(Op("wquant", f"wq {n}x{k}", lambda w32=w32, qw=qw, sw=sw: dg.dg_quantize_per_block(w32, q=qw, sb=sw),
+                      nbytes=quant_bytes(n * k, k)))
+        ops.append(Op("transpose", f"wT {n}x{k}",
+                      lambda qw=qw, sw=sw, qwt=qwt, swt=swt: dg.dg_transpose_blocks(qw, sw, qt=qwt, st=swt),
+                      nbytes=2 * n * k))
+        ops.append(Op("aquant", f"aq X {m}x{k}", lambda x32=x32, qx=qx, sx=sx: dg.dg_quantize_per_token_group(x32, q=qx, sa=sx),
+                      nbytes=quant_bytes(m * k, k)))
+        ops.append(Op("gemm", f"fwd {m}x{n}x{k}",
+                      lambda qx=qx, sx=sx, qw=qw, sw=sw, y=y, ws=ws: dg.dg_gemm_fp8_nt(qx, sx, qw, sw, d=y, workspace=ws),
+                      flops=2.0 * m * n * k, nbytes=dense_gemm_bytes(m, n, k), config=dg.dg_gemm_config_name(0, m, n, k, 1)))
+        ops.append(Op("aquant", f"aq dY {m}x{n}", lambda dy32=dy32, qdy=qdy, sdy=sdy: dg.dg_quantize_per_token_group(dy32, q=qdy, sa=sdy),
+                      nbytes=quant_bytes(m * n, n)))
+        ops.append(Op("gemm", f"dgrad {m}x{k}x{n}",
+                      lambda qdy=qdy, sdy=sdy, qwt=qwt, swt=swt, dx=dx, ws=ws: dg.dg_gemm_fp8_nt(qdy, sdy, qwt, swt, d=dx, workspace=ws),
+                      flops=2.0 * m * n * k, nbytes=dense_gemm_bytes(m, k, n), config=dg.dg_gemm_config_name(0, m, k, n, 1)))
+        ops.append(Op("cquant", f"cq dY {m}x{n}",
+                      lambda dy32=dy32, qdyt=qdyt, sdyt=sdyt: dg.dg_quantize_per_channel_group(dy32, qt=qdyt, st=sdyt),
+                      nbytes=quant_bytes(m * n, m)))
+        ops.append(Op("cquant", f"cq X {m}x{k}",
+                      lambda x32=x32, qxt=qxt, sxt=sxt: dg.dg_quantize_per_channel_group(x32, qt=qxt, st=sxt),
+                      nbytes=quant_bytes(m * k, m)))
+        ops.append(Op("gemm", f"wgrad {n}x{k}x{m}",
+                      lambda qdyt=qdyt, sdyt=sdyt, qxt=qxt, sxt=sxt, dw=dw, ws=ws: dg.dg_gemm_fp8_nt_row_scaled(
+                          qdyt, sdyt, qxt, sxt, d=dw, workspace=ws),
+                      flops=2.0 * m * n * k, nbytes=rowscaled_gemm_bytes(n, k, m),
+                      config="rowscaled " + dg.dg_gemm_config_name(3, n, k, m, 1)))
     return ops
 
 
@@ -210,6 +278,11 @@ def build_workload(name, torch, dg, dev, act_dtype="fp32"):
         desc = ("DeepSeek-V3 dense GEMMs: M in {64,128,4096} x (N,K) in {(2112,7168),(24576,1536),"
                 "(32768,512),(7168,16384),(4096,7168),(7168,2048)}; A~N(0,1) with 1% rows x100, B~N(0,0.02^2)")
         return build_dense(torch, dg, dev, shapes, name, act_dtype), desc
+    if name == "train_v3":
+        return (build_train(torch, dg, dev, 4096, inputs.DENSE_V3_NK),
+                "linear-layer training step at 4096 tokens for each DeepSeek-V3 (N,K) in {(2112,7168),(24576,1536),"
+                "(32768,512),(7168,16384),(4096,7168),(7168,2048)}: forward X W^T, dgrad dY W, wgrad dY^T X; "
+                "X~N(0,1) with 1% rows x100, W~N(0,0.02^2), dY~N(0,0.01^2)")
     if name == "small":
         return build_dense(torch, dg, dev, [(128, 512, 512)], name, act_dtype), "M=128, N=512, K=512"
     if name == "large_dense":
@@ -251,28 +324,39 @@ def cpu_baseline(workload, seconds):
         blas_threads = 1
     # sample: for each (N, K) of the dense V3 set, 64 activation rows x `rows_b` weight rows through
     # the whole oracle path (quantize A rows, quantize B rows, fp64 GEMM); rows_b scaled to the budget
-    nk = inputs.DENSE_V3_NK if workload == "dense_v3" else [(512, 512)]
+    nk = inputs.DENSE_V3_NK if workload in ("dense_v3", "train_v3") else [(512, 512)]
+    train = workload == "train_v3"
     rng = inputs.rng_for("cpu_sample")
 
     def run(rows_b):
         flops, t = 0.0, 0.0
         for (n, k) in nk:
-            a = inputs.activations_with_outliers(rng, 64, k)
+            a = inputs.activations_with_outliers(rng, 128 if train else 64, k)
             b = inputs.normal(rng, (min(rows_b, n), k), 0.02)
             t0 = time.perf_counter()
-            qa, sa = oracle.quant.quantize_per_token_group(a)
-            qb, sb = oracle.quant.quantize_per_block(b)
-            oracle.gemm.gemm_nt(qa, sa, qb, sb)
+            if train:   # forward, dgrad and wgrad of the sampled slice through the oracle
+                dy = inputs.normal(rng, (a.shape[0], b.shape[0]), 1e-2)
+                t0 = time.perf_counter()
+                oracle.train.linear_forward(a, b)
+                oracle.train.linear_dgrad(dy, b)
+                oracle.train.linear_wgrad(dy, a)
+                flops += 3 * 2.0 * a.shape[0] * b.shape[0] * k
+            else:
+                qa, sa = oracle.quant.quantize_per_token_group(a)
+                qb, sb = oracle.quant.quantize_per_block(b)
+                oracle.gemm.gemm_nt(qa, sa, qb, sb)
+                flops += 2.0 * 64 * b.shape[0] * k
             t += time.perf_counter() - t0
-            flops += 2.0 * 64 * b.shape[0] * k
         return flops, t
 
     f0, t0 = run(128)                     # calibration
     rows_b = int(max(128, min(8192, 128 * seconds / max(t0, 1e-3))) // 128 * 128)
     f, t = run(rows_b)
     return {"value": f / t / 1e12, "unit": "TFLOP/s", "cores": int(blas_threads), "kind": "oracle",
-            "sample": (f"oracle quantize + fp64 GEMM of 64 activation rows x {rows_b} weight rows for each (N,K) "
-                       f"of the workload ({f / 1e9:.2f} GFLOP in {t:.1f} s; quantization single-threaded numpy, "
+            "sample": ((f"oracle forward + dgrad + wgrad of 128 tokens x {rows_b} weight rows for each (N,K) "
+                        if train else
+                        f"oracle quantize + fp64 GEMM of 64 activation rows x {rows_b} weight rows for each (N,K) ")
+                       + f"of the workload ({f / 1e9:.2f} GFLOP in {t:.1f} s; quantization single-threaded numpy, "
                        f"GEMM on {blas_threads} BLAS threads)"),
             "seconds": t}
 
@@ -524,7 +608,7 @@ def main():
                 "shapes": sorted({o.label for o in dom_ops})}
 
     quant = {}
-    for kind in ("wquant", "aquant"):
+    for kind in ("wquant", "aquant", "cquant", "transpose"):
         ks = [op for op in ops if op.kind == kind]
         if ks:
             t = sum(float(np.median(o.times)) for o in ks) * 1e-3
@@ -543,7 +627,10 @@ def main():
            "scaling": "weak", "vs_baseline": None, "dtype": "fp8_e4m3", "data": "synthetic",
            "config": {"workload": args.workload, "description": desc, "gemms": len(shapes),
                       "activation_input": args.act_dtype,
-                      "step": "weight quantization (all weights) + per shape: activation quantization, FP8 GEMM",
+                      "step": ("per (N,K): weight quantization + transpose; forward (quantize X, GEMM), dgrad "
+                               "(quantize dY, GEMM with W^T), wgrad (per-channel quantize dY and X, row-scaled GEMM)"
+                               if args.workload == "train_v3" else
+                               "weight quantization (all weights) + per shape: activation quantization, FP8 GEMM"),
                       "timing": "eager" if graph is None else "hip graph replay per step",
                       "device_ms_per_step": round(gpu_ms_per_step, 4),
                       "gemm_only_tflops": round(gemm_flops / (gemm_only_ms * 1e-3) / 1e12, 1),
