@@ -16,7 +16,9 @@ Functions carry the C names:
 * training-side layouts: ``dg_quantize_per_channel_group(x)`` -> (qt uint8 (K, M), st float32
   (ceil(M/128), ld_st)) in groups of 128 tokens per column, transposed (fp32 or bf16 x);
   ``dg_transpose_blocks(q, s)`` -> the block quantization of the transposed matrix;
-  ``dg_gemm_fp8_nt_row_scaled(a, sa, b, sb)`` -> d bf16 (M, N) with per-row scales on both operands
+  ``dg_gemm_fp8_nt_row_scaled(a, sa, b, sb)`` -> d bf16 (M, N) with per-row scales on both operands;
+  ``dg_gemm_fp8_k_grouped_row_scaled(a, sa, b, sb, group_tokens)`` -> d bf16 (G, M, N), the MoE weight
+  gradients over the contiguous layout
 * utilities ``dg_get_num_cus``, ``dg_set_num_cus``,
   ``dg_get_m_alignment_for_contiguous_layout``, ``dg_get_scale_ld``,
   ``dg_gemm_workspace_size``.
@@ -55,6 +57,9 @@ _SIGNATURES = {
                                                   _c_int64, _c_int64, _c_int64, _vp, ctypes.c_size_t, _vp]),
     "dg_gemm_fp8_nt_row_scaled": (ctypes.c_int, [_vp, _vp, _c_int64, _vp, _vp, _c_int64, _vp, _c_int64, _c_int64,
                                                  _c_int64, _vp, ctypes.c_size_t, _vp]),
+    "dg_gemm_fp8_k_grouped_row_scaled": (ctypes.c_int, [_vp, _vp, _c_int64, _vp, _vp, _c_int64, _vp, _vp,
+                                                        _c_int64, _c_int64, _c_int64, _c_int64, _vp, ctypes.c_size_t,
+                                                        _vp]),
     "dg_quantize_per_channel_group": (ctypes.c_int, [_vp, _c_int64, _c_int64, _c_int64, _vp, _vp, _c_int64, _vp]),
     "dg_quantize_per_channel_group_bf16": (ctypes.c_int, [_vp, _c_int64, _c_int64, _c_int64, _vp, _vp, _c_int64,
                                                           _vp]),
@@ -299,6 +304,28 @@ def dg_gemm_fp8_nt_row_scaled(a, sa, b, sb, d=None, workspace=None, use_workspac
     _check("dg_gemm_fp8_nt_row_scaled",
            lib().dg_gemm_fp8_nt_row_scaled(_ptr(a), _ptr(sa), sa.shape[-1], _ptr(b), _ptr(sb), sb.shape[-1], _ptr(d),
                                            m, n, k, _ptr(workspace), ws_bytes, _stream(a)))
+    return d
+
+
+def dg_gemm_fp8_k_grouped_row_scaled(a, sa, b, sb, group_tokens, d=None, workspace=None, use_workspace=True):
+    """MoE weight gradients: a (M, T) and b (N, T) per-channel-quantized over T tokens in the contiguous
+    layout, group_tokens (host sequence of G counts, multiples of 128) -> d bf16 (G, M, N) with
+    d[g] = a[:, seg_g] * b[:, seg_g]^T (zeros for an empty expert)."""
+    a, b = _bytes(a), _bytes(b)
+    m, t = a.shape
+    n = b.shape[0]
+    counts = [int(c) for c in group_tokens]
+    g = len(counts)
+    if d is None:
+        d = torch.empty((g, m, n), dtype=torch.bfloat16, device=a.device)
+    _dev(a, sa, b, sb, d)
+    if workspace is None and use_workspace:
+        workspace = default_workspace(a.device, max([dg_gemm_workspace_size(m, n, c, 1) for c in counts if c] or [0]))
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    arr = (ctypes.c_int64 * max(g, 1))(*counts)
+    _check("dg_gemm_fp8_k_grouped_row_scaled",
+           lib().dg_gemm_fp8_k_grouped_row_scaled(_ptr(a), _ptr(sa), sa.shape[-1], _ptr(b), _ptr(sb), sb.shape[-1],
+                                                  _ptr(d), arr, g, m, n, t, _ptr(workspace), ws_bytes, _stream(a)))
     return d
 
 

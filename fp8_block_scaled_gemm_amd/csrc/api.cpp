@@ -26,8 +26,10 @@ int launch_quant_channel_group_bf16(const uint16_t* x, int64_t mats, int64_t m, 
                                     int64_t ld_st, hipStream_t stream);
 int launch_transpose_blocks(const uint8_t* q, const float* s, int64_t groups, int64_t r, int64_t c, uint8_t* qt,
                             float* st, hipStream_t stream);
+int launch_fill_zero_bf16(uint16_t* d, int64_t count, hipStream_t stream);
 int launch_gemm(int layout, const uint8_t* a, const float* sa, int64_t ld_sa, const uint8_t* b,
-                const float* sb, int64_t ld_sb, uint16_t* d, const int32_t* m_indices, const int32_t* masked_m,
+                const float* sb, int64_t ld_sb, int64_t ld_ab, uint16_t* d, const int32_t* m_indices,
+                const int32_t* masked_m,
                 int64_t groups, int64_t m, int64_t n, int64_t k, void* ws, size_t ws_bytes,
                 hipStream_t stream, int num_cus);
 size_t gemm_workspace_size(int64_t m, int64_t n, int64_t k, int64_t groups, int num_cus);
@@ -176,7 +178,7 @@ int dg_gemm_fp8_nt(const uint8_t* a, const float* sa, int64_t ld_sa, const uint8
   DG_REQUIRE(workspace == nullptr || aligned16(workspace), "gemm: workspace must be 16-byte aligned");
   const int cus = effective_cus();
   if (cus < 0) return cus;
-  return launch_gemm(0, a, sa, ld_sa, b, sb, 0, d, nullptr, nullptr, 1, m, n, k, workspace,
+  return launch_gemm(0, a, sa, ld_sa, b, sb, 0, 0, d, nullptr, nullptr, 1, m, n, k, workspace,
                      workspace ? workspace_bytes : 0, static_cast<hipStream_t>(stream), cus);
 }
 
@@ -192,7 +194,7 @@ int dg_gemm_fp8_grouped_contiguous(const uint8_t* a, const float* sa, int64_t ld
   DG_REQUIRE(m_indices != nullptr, "contiguous gemm: m_indices is null");
   const int cus = effective_cus();
   if (cus < 0) return cus;
-  return launch_gemm(1, a, sa, ld_sa, b, sb, 0, d, m_indices, nullptr, num_groups, m_total, n, k,
+  return launch_gemm(1, a, sa, ld_sa, b, sb, 0, 0, d, m_indices, nullptr, num_groups, m_total, n, k,
                      nullptr, 0, static_cast<hipStream_t>(stream), cus);
 }
 
@@ -210,7 +212,7 @@ int dg_gemm_fp8_grouped_masked(const uint8_t* a, const float* sa, int64_t ld_sa,
   DG_REQUIRE(workspace == nullptr || aligned16(workspace), "gemm: workspace must be 16-byte aligned");
   const int cus = effective_cus();
   if (cus < 0) return cus;
-  return launch_gemm(2, a, sa, ld_sa, b, sb, 0, d, nullptr, masked_m, num_groups, m_max, n, k,
+  return launch_gemm(2, a, sa, ld_sa, b, sb, 0, 0, d, nullptr, masked_m, num_groups, m_max, n, k,
                      workspace, workspace ? workspace_bytes : 0, static_cast<hipStream_t>(stream), cus);
 }
 
@@ -224,8 +226,50 @@ int dg_gemm_fp8_nt_row_scaled(const uint8_t* a, const float* sa, int64_t ld_sa, 
   DG_REQUIRE(workspace == nullptr || aligned16(workspace), "gemm: workspace must be 16-byte aligned");
   const int cus = effective_cus();
   if (cus < 0) return cus;
-  return launch_gemm(3, a, sa, ld_sa, b, sb, ld_sb, d, nullptr, nullptr, 1, m, n, k, workspace,
+  return launch_gemm(3, a, sa, ld_sa, b, sb, ld_sb, 0, d, nullptr, nullptr, 1, m, n, k, workspace,
                      workspace ? workspace_bytes : 0, static_cast<hipStream_t>(stream), cus);
+}
+
+int dg_gemm_fp8_k_grouped_row_scaled(const uint8_t* a, const float* sa, int64_t ld_sa, const uint8_t* b,
+                                     const float* sb, int64_t ld_sb, uint16_t* d, const int64_t* group_tokens,
+                                     int64_t num_groups, int64_t m, int64_t n, int64_t tokens_total, void* workspace,
+                                     size_t workspace_bytes, dg_stream_t stream) {
+  DG_REQUIRE(num_groups >= 0 && m >= 0 && n >= 0 && tokens_total >= 0,
+             "k-grouped gemm: negative size (groups=%lld m=%lld n=%lld tokens=%lld)", (long long)num_groups,
+             (long long)m, (long long)n, (long long)tokens_total);
+  if (num_groups == 0 || m == 0 || n == 0) return DG_OK;
+  DG_REQUIRE(group_tokens != nullptr, "k-grouped gemm: group_tokens is null");
+  int64_t total = 0;
+  for (int64_t g = 0; g < num_groups; ++g) {
+    DG_REQUIRE(group_tokens[g] >= 0 && group_tokens[g] % kGroup == 0,
+               "k-grouped gemm: group %lld has %lld tokens (need a multiple of 128)", (long long)g,
+               (long long)group_tokens[g]);
+    total += group_tokens[g];
+  }
+  DG_REQUIRE(total == tokens_total, "k-grouped gemm: group tokens sum to %lld, tokens_total is %lld", (long long)total,
+             (long long)tokens_total);
+  DG_REQUIRE(a && sa && b && sb && d, "k-grouped gemm: null pointer");
+  DG_REQUIRE(aligned16(a) && aligned16(sa) && aligned16(b) && aligned16(sb) && aligned16(d),
+             "k-grouped gemm: pointers must be 16-byte aligned");
+  DG_REQUIRE(ld_sa >= m && ld_sa % 4 == 0 && ld_sb >= n && ld_sb % 4 == 0,
+             "k-grouped gemm: need ld_sa >= m, ld_sb >= n, both multiples of 4");
+  DG_REQUIRE((m * n) % 8 == 0, "k-grouped gemm: m * n must be a multiple of 8 (16-byte output blocks)");
+  DG_REQUIRE(workspace == nullptr || aligned16(workspace), "gemm: workspace must be 16-byte aligned");
+  const int cus = effective_cus();
+  if (cus < 0) return cus;
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  int64_t start = 0;
+  for (int64_t g = 0; g < num_groups; ++g) {
+    const int64_t tk = group_tokens[g];
+    uint16_t* dg_ = d + g * m * n;
+    const int r = tk == 0 ? launch_fill_zero_bf16(dg_, m * n, s)
+                          : launch_gemm(3, a + start, sa + (start / kGroup) * ld_sa, ld_sa, b + start,
+                                        sb + (start / kGroup) * ld_sb, ld_sb, tokens_total, dg_, nullptr, nullptr, 1,
+                                        m, n, tk, workspace, workspace ? workspace_bytes : 0, s, cus);
+    if (r != kOk) return r;
+    start += tk;
+  }
+  return DG_OK;
 }
 
 static int check_channel_group(const void* x, int64_t num_groups, int64_t m, int64_t k, uint8_t* qt, float* st,

@@ -229,12 +229,16 @@ __global__ __launch_bounds__(C::kThreads) void gemm_fp8_kernel(GemmParams p) {
     constexpr int kBandsB = C::kDmaB / C::kWaves;
     const int dma_row = 8 * wave + (lane >> 3);   // tile-local row within band 0 (f(row) is band-invariant)
     const int dma_chunk = ((lane & 7) ^ swz_row(dma_row)) << 4;   // byte offset of this lane's chunk in the K block
-    const uint32_t dma_off = (uint32_t)dma_row * (uint32_t)p.k + (uint32_t)dma_chunk;
-    const uint32_t band_step = (uint32_t)kBandRows * (uint32_t)p.k;
+    // Operand rows are ld bytes apart: k, except for kDenseRowB on a K slice of wider matrices
+    // (the per-expert token ranges of the grouped weight gradient).  A resource ends after the last
+    // present row's k bytes, so rows past the edge read zeros.
+    const int ld = kRowB ? p.ld_ab : p.k;
+    const uint32_t dma_off = (uint32_t)dma_row * (uint32_t)ld + (uint32_t)dma_chunk;
+    const uint32_t band_step = (uint32_t)kBandRows * (uint32_t)ld;
     const __amdgpu_buffer_rsrc_t rs_b =
-        make_rsrc(b_g + (int64_t)n0 * p.k, p.n > n0 ? (int64_t)(p.n - n0) * p.k : 0);
+        make_rsrc(b_g + (int64_t)n0 * ld, p.n > n0 ? (int64_t)(p.n - n0 - 1) * ld + p.k : 0);
     const __amdgpu_buffer_rsrc_t rs_a =
-        make_rsrc(a_g + (int64_t)m0 * p.k, p.m > m0 ? (int64_t)(p.m - m0) * p.k : 0);
+        make_rsrc(a_g + (int64_t)m0 * ld, p.m > m0 ? (int64_t)(p.m - m0 - 1) * ld + p.k : 0);
     // activation scales: lanes [kSaLanesPerWave*wave, +kSaLanesPerWave) of the BM/4 16-byte chunks
     // of sa[kb][m0 .. m0+BM); chunks are clamped to the caller's ld_sa row (rows >= m are never stored)
     const int sa_lane = wave * C::kSaLanesPerWave + lane;
@@ -674,12 +678,13 @@ static int launch_layout(GemmParams p, const Plan& pl, hipStream_t stream, int n
 }
 
 int launch_gemm(int layout, const uint8_t* a, const float* sa, int64_t ld_sa, const uint8_t* b,
-                const float* sb, int64_t ld_sb, uint16_t* d, const int32_t* m_indices, const int32_t* masked_m,
-                int64_t groups, int64_t m, int64_t n, int64_t k, void* ws, size_t ws_bytes,
+                const float* sb, int64_t ld_sb, int64_t ld_ab, uint16_t* d, const int32_t* m_indices,
+                const int32_t* masked_m, int64_t groups, int64_t m, int64_t n, int64_t k, void* ws, size_t ws_bytes,
                 hipStream_t stream, int num_cus) {
-  if (n * k > 0x7fffffffLL || m * k > 0x7fffffffLL)
-    return set_error(kUnsupported, "gemm: one group's operand must be < 2^31 bytes (m=%lld n=%lld k=%lld)",
-                     (long long)m, (long long)n, (long long)k);
+  const int64_t ld = ld_ab > 0 ? ld_ab : k;   // operand row stride (bytes)
+  if (n * ld > 0x7fffffffLL || m * ld > 0x7fffffffLL)
+    return set_error(kUnsupported, "gemm: one group's operand must be < 2^31 bytes (m=%lld n=%lld k=%lld ld=%lld)",
+                     (long long)m, (long long)n, (long long)k, (long long)ld);
   if (layout == kMasked && groups > 1024) return set_error(kUnsupported, "masked gemm: at most 1024 groups");
   const int64_t tile_groups = layout == kMasked ? groups : 1;
   const bool can_split = (layout != kContiguous) && ws != nullptr;
@@ -691,6 +696,7 @@ int launch_gemm(int layout, const uint8_t* a, const float* sa, int64_t ld_sa, co
   p.m_indices = m_indices; p.masked_m = masked_m;
   p.ld_sa = ld_sa;
   p.ld_sb = ld_sb;
+  p.ld_ab = (int)ld;
   p.m = (int)m; p.n = (int)n; p.k = (int)k;
   p.num_groups = (int)(layout == kDense || layout == kDenseRowB ? 1 : groups);
   p.kb_total = (int)((k + kGroup - 1) / kGroup);
@@ -712,6 +718,23 @@ int launch_gemm(int layout, const uint8_t* a, const float* sa, int64_t ld_sa, co
     case kDenseRowB: return launch_layout<kDenseRowB>(p, pl, stream, num_cus);
     default: return launch_layout<kDense>(p, pl, stream, num_cus);
   }
+}
+
+// bf16 zero fill of count elements (count % 8 == 0, 16-byte aligned): the weight gradient of an
+// expert that received no tokens.
+__global__ __launch_bounds__(256) void fill_zero_kernel(uint16_t* d, int64_t chunks) {
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < chunks; i += (int64_t)gridDim.x * 256)
+    reinterpret_cast<u32x4*>(d)[i] = u32x4{0u, 0u, 0u, 0u};
+}
+
+int launch_fill_zero_bf16(uint16_t* d, int64_t count, hipStream_t stream) {
+  const int64_t chunks = count / 8;
+  if (chunks <= 0) return kOk;
+  int64_t blocks = (chunks + 255) / 256;
+  if (blocks > 4096) blocks = 4096;
+  hipLaunchKernelGGL(fill_zero_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, d, chunks);
+  const hipError_t e = hipGetLastError();
+  return e == hipSuccess ? kOk : set_error(kHip, "zero fill launch: %s", hipGetErrorString(e));
 }
 
 }  // namespace dg

@@ -25,6 +25,7 @@ struct GemmParams {
   unsigned* counters;         // split-K arrival counters, one per output tile
   int64_t ld_sa;
   int64_t ld_sb;             // kDenseRowB: row stride of the per-row B scales
+  int ld_ab;                 // kDenseRowB: row stride (bytes) of both operands (k, or larger for K slices)
   int64_t a_gstride, sa_gstride, b_gstride, sb_gstride, d_gstride;   // per-group strides (elements)
   int m;            // rows per group (dense: M, contiguous: M_total, masked: M_max)
   int n, k;

@@ -183,7 +183,8 @@ int dg_gemm_fp8_grouped_masked(const uint8_t* a, const float* sa, int64_t ld_sa,
  *   dgrad  dX = dY * W       = dg_gemm_fp8_nt(dY per-token groups, W^T blocks)
  *          (W^T's 128 x 128 block quantization is W's transposed: dg_transpose_blocks);
  *   wgrad  dW = dY^T * X     = dg_gemm_fp8_nt_row_scaled(dY^T, X^T), both operands in
- *          groups of 128 tokens per column (dg_quantize_per_channel_group).
+ *          groups of 128 tokens per column (dg_quantize_per_channel_group);
+ *          per expert over the contiguous MoE layout: dg_gemm_fp8_k_grouped_row_scaled.
  */
 
 /*
@@ -230,6 +231,25 @@ int dg_transpose_blocks(const uint8_t* q, const float* s, int64_t num_groups, in
 int dg_gemm_fp8_nt_row_scaled(const uint8_t* a, const float* sa, int64_t ld_sa, const uint8_t* b,
                               const float* sb, int64_t ld_sb, uint16_t* d, int64_t m, int64_t n, int64_t k,
                               void* workspace, size_t workspace_bytes, dg_stream_t stream);
+
+/*
+ * MoE weight gradients over the contiguous layout (the layout the pages name for MoE training
+ * forward: 3loumao explainer, section 03): expert g's tokens are columns [start_g, start_g + T_g)
+ * of both operands, start_g = T_0 + ... + T_{g-1}, and D[g] = A_g * B_g^T with per-row group
+ * scales on both (dW_g = dY_g^T X_g from dg_quantize_per_channel_group of the whole dY and X:
+ * every T_g is a multiple of 128, so no 128-token group straddles two experts).
+ * a  : E4M3 (m, tokens_total) row-major;  sa : fp32 sa[tb * ld_sa + row], tb = token group.
+ * b  : E4M3 (n, tokens_total) row-major;  sb : fp32 sb[tb * ld_sb + col].
+ * d  : bf16 (num_groups, m, n), written; an expert with T_g = 0 gets zeros.
+ * group_tokens : int64 (num_groups,), HOST memory, each a multiple of 128, summing to tokens_total.
+ * workspace : as dg_gemm_fp8_nt, shared by the experts' GEMMs (run in order on `stream`).
+ * Errors: DG_ERR_INVALID_ARG for null/misaligned pointers, negative sizes, a count that is not a
+ * multiple of 128, counts not summing to tokens_total, ld_sa < m, ld_sb < n, m * n % 8 != 0.
+ */
+int dg_gemm_fp8_k_grouped_row_scaled(const uint8_t* a, const float* sa, int64_t ld_sa, const uint8_t* b,
+                                     const float* sb, int64_t ld_sb, uint16_t* d, const int64_t* group_tokens,
+                                     int64_t num_groups, int64_t m, int64_t n, int64_t tokens_total, void* workspace,
+                                     size_t workspace_bytes, dg_stream_t stream);
 
 /*
  * Utilities (CSDN article, "utilities": cap on the compute units used,

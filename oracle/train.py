@@ -96,3 +96,23 @@ def linear_wgrad(dy, x):
     qa, sa = quantize_per_channel_group(dy)
     qb, sb = quantize_per_channel_group(x)
     return gemm_nt_row_scaled(qa, sa, qb, sb)
+
+
+def linear_wgrad_k_grouped(dy, x, group_tokens):
+    """MoE weight gradients over the contiguous layout (the layout the pages name for MoE training
+    forward): expert e's tokens are rows [start_e, start_e + T_e) of dY (M, N) and X (M, K), with
+    start_e the sum of the earlier counts; dW_e = dY_e^T X_e, returned as (G, N, K) fp64, zero for an
+    expert with no tokens.  Every T_e is a multiple of 128 (the layout's alignment), so no 128-token
+    group straddles two experts: quantizing the whole matrices per channel gives each expert's
+    operands exactly (reading O22)."""
+    dy = np.asarray(dy, dtype=np.float32)
+    x = np.asarray(x, dtype=np.float32)
+    n, k = dy.shape[1], x.shape[1]
+    out = np.zeros((len(group_tokens), n, k))
+    start = 0
+    for e, t in enumerate(group_tokens):
+        assert t % GROUP == 0, "expert token counts must be multiples of 128"
+        if t:
+            out[e] = linear_wgrad(dy[start:start + t], x[start:start + t])
+        start += t
+    return out

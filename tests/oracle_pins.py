@@ -627,6 +627,37 @@ def pin_linear_layer_identities(seed=73):
     assert np.array_equal(oracle.train.linear_wgrad(dy, x), dy64.T @ x64)
 
 
+def pin_k_grouped_wgrad_exact(seed=79):
+    """MoE wgrad over the contiguous layout on exactly quantizable operands: each expert's dW_e must
+    equal the exact product of its own token rows (an empty expert gives zeros), so a shifted,
+    swapped or dropped segment fails."""
+    rng = np.random.default_rng(seed)
+    tokens = [256, 0, 128, 384]
+    m, n, k = sum(tokens), 136, 128
+    x = _exactly_quantizable(rng, m, k)
+    dy = _exactly_quantizable(rng, m, n)
+    got = oracle.train.linear_wgrad_k_grouped(dy, x, tokens)
+    assert got.shape == (4, n, k)
+    start = 0
+    for e, t in enumerate(tokens):
+        ref = dy[start:start + t].astype(np.float64).T @ x[start:start + t].astype(np.float64)
+        assert np.array_equal(got[e], ref), e
+        start += t
+
+
+def pin_k_grouped_wgrad_sums_to_dense(seed=83):
+    """The experts' weight gradients sum to the dense weight gradient over all tokens (128-aligned
+    segments: the per-channel groups of the whole matrix are the experts' groups)."""
+    rng = np.random.default_rng(seed)
+    tokens = [128, 384, 256]
+    m = sum(tokens)
+    x = (rng.standard_normal((m, 96)) * np.exp2(rng.uniform(-3, 3, size=(m, 1)))).astype(np.float32)
+    dy = rng.standard_normal((m, 80)).astype(np.float32)
+    per_expert = oracle.train.linear_wgrad_k_grouped(dy, x, tokens)
+    dense = oracle.train.linear_wgrad(dy, x)
+    assert np.allclose(per_expert.sum(axis=0), dense, rtol=1e-12, atol=1e-12 * np.abs(dense).max())
+
+
 ALL_PINS = [
     pin_e4m3_named_codes, pin_e4m3_decode_vs_torch, pin_e4m3_roundtrip, pin_e4m3_encode_vs_torch,
     pin_e4m3_ties_and_saturation, pin_e4m3_brute_force_sample,
@@ -638,5 +669,5 @@ ALL_PINS = [
     pin_quant_ragged_k, pin_gemm_ragged_k_exact,
     pin_channel_quant_brute_force, pin_channel_quant_is_token_quant_of_transpose, pin_channel_quant_bf16_widening,
     pin_block_quant_commutes_with_transpose, pin_row_scaled_gemm_exact, pin_row_scaled_reduces_to_block_scaled,
-    pin_linear_layer_identities,
+    pin_linear_layer_identities, pin_k_grouped_wgrad_exact, pin_k_grouped_wgrad_sums_to_dense,
 ]

@@ -130,3 +130,17 @@ def test_training_layout_argument_validation(lib):
     assert lib.dg_gemm_fp8_nt_row_scaled(*rs(8, 8, 128, 4, 8)) == DG_ERR_INVALID_ARG     # ld_sa < m
     assert lib.dg_gemm_fp8_nt_row_scaled(*rs(4, 8, 128, 4, 8, a=None)) == DG_ERR_INVALID_ARG
     assert lib.dg_gemm_fp8_nt_row_scaled(*rs(0, 8, 128, 0, 8, a=None)) == DG_OK           # empty: no-op
+
+
+def test_k_grouped_argument_validation(lib):
+    fake = _p(0x1000)
+    counts = lambda *c: (ctypes.c_int64 * len(c))(*c)
+    kg = lambda cnt, g, total, ld_sa=8, ld_sb=8, m=8, n=8: (fake, fake, ld_sa, fake, fake, ld_sb, fake, cnt, g, m, n,
+                                                             total, None, 0, None)
+    assert lib.dg_gemm_fp8_k_grouped_row_scaled(*kg(counts(128, 100), 2, 228)) == DG_ERR_INVALID_ARG   # 100 % 128
+    assert lib.dg_gemm_fp8_k_grouped_row_scaled(*kg(counts(128, 256), 2, 256)) == DG_ERR_INVALID_ARG   # sum != total
+    assert lib.dg_gemm_fp8_k_grouped_row_scaled(*kg(counts(128, -128), 2, 0)) == DG_ERR_INVALID_ARG    # negative
+    assert lib.dg_gemm_fp8_k_grouped_row_scaled(*kg(None, 2, 256)) == DG_ERR_INVALID_ARG               # no counts
+    assert lib.dg_gemm_fp8_k_grouped_row_scaled(*kg(counts(128), 1, 128, ld_sa=4)) == DG_ERR_INVALID_ARG  # ld_sa < m
+    assert lib.dg_gemm_fp8_k_grouped_row_scaled(*kg(counts(128), 1, 128, m=3, n=5, ld_sa=4)) == DG_ERR_INVALID_ARG  # m*n % 8
+    assert lib.dg_gemm_fp8_k_grouped_row_scaled(*kg(None, 0, 0)) == DG_OK                                # no groups

@@ -194,3 +194,50 @@ def test_wgrad_full_size_sampled_rows():
     assert np.array_equal(qxt.cpu().numpy(), qb_o)
     assert np.array_equal(bits32(sxt[:, :k].T.contiguous().cpu().numpy()), bits32(sb_o))
     check_gemm(dw[ridx], oracle.train.gemm_nt_row_scaled(qa_o, sa_o, qb_o, sb_o), "wgrad sampled rows")
+
+
+@pytest.mark.parametrize("tokens,n,k", [([256, 0, 128, 640], 256, 384), ([512] * 3 + [384, 640, 128, 0, 768], 512, 1024),
+                                        ([128], 136, 200)])
+def test_moe_wgrad_k_grouped(tokens, n, k):
+    """dW_e = dY_e^T X_e per expert over the contiguous layout through the library (per-channel
+    quantization of the whole dY and X, then the k-grouped row-scaled GEMM) against the oracle; an
+    expert with no tokens gets zeros (the output is pre-filled with NaN)."""
+    t = sum(tokens)
+    say("moe wgrad k-grouped", tokens, n, k)
+    rng = inputs.rng_for("moe_wgrad", t, n, k)
+    x = inputs.activations_with_outliers(rng, t, k)
+    dy = inputs.normal(rng, (t, n), 1e-2)
+    qdyt, sdyt = dg.dg_quantize_per_channel_group(to_dev(dy))
+    qxt, sxt = dg.dg_quantize_per_channel_group(to_dev(x))
+    d = torch.full((len(tokens), n, k), float("nan"), dtype=torch.bfloat16, device=device())
+    dg.dg_gemm_fp8_k_grouped_row_scaled(qdyt, sdyt, qxt, sxt, tokens, d=d)
+    torch.cuda.synchronize()
+    ref = oracle.train.linear_wgrad_k_grouped(dy, x, tokens)
+    for e, te in enumerate(tokens):
+        if te == 0:
+            assert bool(torch.all(d[e] == 0)), f"empty expert {e} not zeroed"
+        else:
+            check_gemm(d[e], ref[e], f"expert {e} ({te} tokens)")
+
+
+def test_moe_dgrad_contiguous():
+    """dX = dY W_e per token over the contiguous layout: the contiguous-grouped GEMM on the experts'
+    transposed weight blocks (dg_transpose_blocks of the (G, N, K) block quantization)."""
+    g, n, k = 4, 384, 256
+    sizes = [200, 0, 77, 300]
+    m_idx, starts, valid = inputs.contiguous_layout(sizes)
+    m_total = m_idx.shape[0]
+    say("moe dgrad contiguous", sizes, n, k)
+    rng = inputs.rng_for("moe_dgrad", n, k)
+    w = inputs.normal(rng, (g, n, k), 0.02)
+    dy = inputs.normal(rng, (m_total, n), 1e-2) * valid[:, None].astype(np.float32)
+    qw, sw = dg.dg_quantize_per_block(to_dev(w))
+    qwt, swt = dg.dg_transpose_blocks(qw, sw)
+    qdy, sdy = dg.dg_quantize_per_token_group(to_dev(dy))
+    dx = dg.dg_gemm_fp8_grouped_contiguous(qdy, sdy, qwt, swt, torch.from_numpy(m_idx).to(device()))
+    torch.cuda.synchronize()
+    qa, sa = oracle.quant.quantize_per_token_group(dy)
+    tq = [oracle.train.transpose_blocks(*oracle.quant.quantize_per_block(w[e])) for e in range(g)]
+    ref = oracle.gemm.gemm_grouped_contiguous(qa, sa, np.stack([q for q, _ in tq]), np.stack([s for _, s in tq]), m_idx)
+    rows = np.nonzero(m_idx >= 0)[0]
+    check_gemm(dx[torch.as_tensor(rows, device=device())], ref[rows], "moe dgrad")

@@ -151,6 +151,7 @@ def _quant_tail_scale_from_full_window(x):
 
 _orig_channel = T.quantize_per_channel_group
 _orig_wgrad = T.linear_wgrad
+_orig_kgrouped = T.linear_wgrad_k_grouped
 
 def _channel_quant_whole_column(x):
     """Per-channel quantizer with one scale over the whole column instead of per 128 tokens."""
@@ -181,6 +182,16 @@ def _wgrad_swapped(dy, x):
     return _orig_wgrad(x, dy)
 
 
+def _k_grouped_experts_reversed(dy, x, group_tokens):
+    return _orig_kgrouped(dy, x, group_tokens)[::-1].copy()
+
+
+def _k_grouped_segment_shifted(dy, x, group_tokens):
+    """Every expert's segment starts 128 tokens late (wrapping): the classic off-by-one-group slip."""
+    shift = 128
+    return _orig_kgrouped(np.roll(dy, -shift, axis=0), np.roll(x, -shift, axis=0), group_tokens)
+
+
 _orig_gemm_nt = G.gemm_nt
 _orig_tok = Q.quantize_per_token_group
 
@@ -207,6 +218,8 @@ MUTANTS = {
     "transpose_blocks_keeps_scales": (T, "transpose_blocks", _transpose_blocks_keeps_scales),
     "row_scaled_gemm_block_index": (T, "gemm_nt_row_scaled", _row_scaled_uses_block_index),
     "wgrad_operands_swapped": (T, "linear_wgrad", _wgrad_swapped),
+    "k_grouped_experts_reversed": (T, "linear_wgrad_k_grouped", _k_grouped_experts_reversed),
+    "k_grouped_segment_shifted": (T, "linear_wgrad_k_grouped", _k_grouped_segment_shifted),
 }
 
 
