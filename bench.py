@@ -1,7 +1,7 @@
 """Benchmark of the FP8 block-scaled GEMM hot path on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload dense_v3|small|contiguous|masked|
-                     large_dense|zipf|train_v3|overlap] [--no-cpu-baseline] [--cpu-seconds S] [--eager]
+                     large_dense|zipf|train_v3|train_moe|overlap] [--no-cpu-baseline] [--cpu-seconds S] [--eager]
     python bench.py --copy-calibration      # counter calibration: one plain 1 GiB device copy
 
 One step is one pass of the whole hot path over one batch of synthetic input:
@@ -56,7 +56,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="dense_v3",
                     choices=["dense_v3", "small", "contiguous", "masked", "large_dense", "zipf", "train_v3",
-                             "overlap"])
+                             "train_moe", "overlap"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target CPU work of the oracle sample")
     ap.add_argument("--eager", action="store_true", help="time eager launches instead of graph replays")
@@ -234,6 +234,77 @@ def build_contiguous(torch, dg, dev, cases):
     return ops
 
 
+def build_train_moe(torch, dg, dev, cases):
+    """MoE layer training step over the contiguous layout, per case (sizes, n, k): forward (contiguous
+    GEMM), dgrad (contiguous GEMM on the experts' transposed weight blocks) and wgrad (per-channel
+    quantization of the whole dY and X, then the k-grouped row-scaled GEMM per expert)."""
+    from fp8_block_scaled_gemm_amd import inputs
+    gen = Gen(torch, dev, 5678)
+    ops = []
+    u8, f32 = torch.uint8, torch.float32
+    for sizes, n, k in cases:
+        g = len(sizes)
+        m_idx_np, starts, valid_np = inputs.contiguous_layout(sizes)
+        m_total = m_idx_np.shape[0]
+        padded = [int(c) for c in np.diff(np.append(starts, m_total))]
+        rows = int(np.sum(sizes))
+        valid = torch.from_numpy(valid_np).to(dev).float()[:, None]
+        w32 = gen.normal((g, n, k), 0.02)
+        x32 = gen.activations(m_total, k) * valid
+        dy32 = gen.normal((m_total, n), 1e-2) * valid
+        m_idx = torch.from_numpy(m_idx_np).to(dev)
+        qw = torch.empty((g, n, k), dtype=u8, device=dev)
+        sw = torch.empty((g, -(-n // 128), -(-k // 128)), dtype=f32, device=dev)
+        qwt = torch.empty((g, k, n), dtype=u8, device=dev)
+        swt = torch.empty((g, -(-k // 128), -(-n // 128)), dtype=f32, device=dev)
+        qx = torch.empty((m_total, k), dtype=u8, device=dev)
+        sx = torch.empty((-(-k // 128), dg.dg_get_scale_ld(m_total)), dtype=f32, device=dev)
+        qdy = torch.empty((m_total, n), dtype=u8, device=dev)
+        sdy = torch.empty((-(-n // 128), dg.dg_get_scale_ld(m_total)), dtype=f32, device=dev)
+        qdyt = torch.empty((n, m_total), dtype=u8, device=dev)
+        sdyt = torch.empty((m_total // 128, dg.dg_get_scale_ld(n)), dtype=f32, device=dev)
+        qxt = torch.empty((k, m_total), dtype=u8, device=dev)
+        sxt = torch.empty((m_total // 128, dg.dg_get_scale_ld(k)), dtype=f32, device=dev)
+        y = torch.empty((m_total, n), dtype=torch.bfloat16, device=dev)
+        dx = torch.empty((m_total, k), dtype=torch.bfloat16, device=dev)
+        dw = torch.empty((g, n, k), dtype=torch.bfloat16, device=dev)
+        ws = dg.default_workspace(dev, max([dg.dg_gemm_workspace_size(n, k, c, 1) for c in padded if c] or [0]))
+        tag = f"G={g} rows={rows} N={n} K={k}"
+        ops.append(Op("wquant", f"wq {g}x{n}x{k}", lambda w32=w32, qw=qw, sw=sw: dg.dg_quantize_per_block(w32, q=qw, sb=sw),
+                      nbytes=quant_bytes(g * n * k, k)))
+        ops.append(Op("transpose", f"wT {g}x{n}x{k}",
+                      lambda qw=qw, sw=sw, qwt=qwt, swt=swt: dg.dg_transpose_blocks(qw, sw, qt=qwt, st=swt),
+                      nbytes=2 * g * n * k))
+        ops.append(Op("aquant", f"aq X {m_total}x{k}", lambda x32=x32, qx=qx, sx=sx: dg.dg_quantize_per_token_group(x32, q=qx, sa=sx),
+                      nbytes=quant_bytes(m_total * k, k)))
+        ops.append(Op("gemm", f"fwd {tag}",
+                      lambda qx=qx, sx=sx, qw=qw, sw=sw, m_idx=m_idx, y=y: dg.dg_gemm_fp8_grouped_contiguous(qx, sx, qw, sw, m_idx, d=y),
+                      flops=2.0 * rows * n * k,
+                      nbytes=m_total * k + g * n * k + 2 * m_total * n + 4 * m_total * (k // 128) + 4 * m_total,
+                      config=dg.dg_gemm_config_name(1, m_total, n, k, g)))
+        ops.append(Op("aquant", f"aq dY {m_total}x{n}", lambda dy32=dy32, qdy=qdy, sdy=sdy: dg.dg_quantize_per_token_group(dy32, q=qdy, sa=sdy),
+                      nbytes=quant_bytes(m_total * n, n)))
+        ops.append(Op("gemm", f"dgrad {tag}",
+                      lambda qdy=qdy, sdy=sdy, qwt=qwt, swt=swt, m_idx=m_idx, dx=dx: dg.dg_gemm_fp8_grouped_contiguous(
+                          qdy, sdy, qwt, swt, m_idx, d=dx),
+                      flops=2.0 * rows * n * k,
+                      nbytes=m_total * n + g * n * k + 2 * m_total * k + 4 * m_total * (n // 128) + 4 * m_total,
+                      config=dg.dg_gemm_config_name(1, m_total, k, n, g)))
+        ops.append(Op("cquant", f"cq dY {m_total}x{n}",
+                      lambda dy32=dy32, qdyt=qdyt, sdyt=sdyt: dg.dg_quantize_per_channel_group(dy32, qt=qdyt, st=sdyt),
+                      nbytes=quant_bytes(m_total * n, m_total)))
+        ops.append(Op("cquant", f"cq X {m_total}x{k}",
+                      lambda x32=x32, qxt=qxt, sxt=sxt: dg.dg_quantize_per_channel_group(x32, qt=qxt, st=sxt),
+                      nbytes=quant_bytes(m_total * k, m_total)))
+        ops.append(Op("gemm", f"wgrad {tag}",
+                      lambda qdyt=qdyt, sdyt=sdyt, qxt=qxt, sxt=sxt, dw=dw, ws=ws, padded=padded:
+                      dg.dg_gemm_fp8_k_grouped_row_scaled(qdyt, sdyt, qxt, sxt, padded, d=dw, workspace=ws),
+                      flops=2.0 * rows * n * k,
+                      nbytes=(n + k) * m_total + 4 * (n + k) * (m_total // 128) + 2 * g * n * k,
+                      config="kgrouped " + dg.dg_gemm_config_name(3, n, k, max(padded), 1)))
+    return ops
+
+
 def build_masked(torch, dg, dev, cases):
     """cases: list of (masked_m np int32 array, m_max, n, k)."""
     gen = Gen(torch, dev, 999)
@@ -283,6 +354,11 @@ def build_workload(name, torch, dg, dev, act_dtype="fp32"):
                 "linear-layer training step at 4096 tokens for each DeepSeek-V3 (N,K) in {(2112,7168),(24576,1536),"
                 "(32768,512),(7168,16384),(4096,7168),(7168,2048)}: forward X W^T, dgrad dY W, wgrad dY^T X; "
                 "X~N(0,1) with 1% rows x100, W~N(0,0.02^2), dY~N(0,0.01^2)")
+    if name == "train_moe":
+        sizes = inputs.uniform_group_sizes(inputs.rng_for("contiguous", 8), 8)
+        return (build_train_moe(torch, dg, dev, [(sizes, n, k) for (n, k) in inputs.GROUPED_NK]),
+                "MoE layer training step over the contiguous layout: G=8, ~8192 tokens/expert (+-25%) padded to 128, "
+                "(N,K) in {(4096,7168),(7168,2048)}: forward, dgrad (transposed expert blocks), wgrad (k-grouped)")
     if name == "small":
         return build_dense(torch, dg, dev, [(128, 512, 512)], name, act_dtype), "M=128, N=512, K=512"
     if name == "large_dense":
@@ -324,8 +400,9 @@ def cpu_baseline(workload, seconds):
         blas_threads = 1
     # sample: for each (N, K) of the dense V3 set, 64 activation rows x `rows_b` weight rows through
     # the whole oracle path (quantize A rows, quantize B rows, fp64 GEMM); rows_b scaled to the budget
-    nk = inputs.DENSE_V3_NK if workload in ("dense_v3", "train_v3") else [(512, 512)]
-    train = workload == "train_v3"
+    nk = (inputs.DENSE_V3_NK if workload in ("dense_v3", "train_v3") else
+          inputs.GROUPED_NK if workload == "train_moe" else [(512, 512)])
+    train = workload in ("train_v3", "train_moe")
     rng = inputs.rng_for("cpu_sample")
 
     def run(rows_b):
@@ -630,6 +707,9 @@ def main():
                       "step": ("per (N,K): weight quantization + transpose; forward (quantize X, GEMM), dgrad "
                                "(quantize dY, GEMM with W^T), wgrad (per-channel quantize dY and X, row-scaled GEMM)"
                                if args.workload == "train_v3" else
+                               "per (N,K): expert weight quantization + transpose; forward (quantize X, contiguous GEMM), "
+                               "dgrad (quantize dY, contiguous GEMM with W_e^T), wgrad (per-channel quantize dY and X, "
+                               "k-grouped row-scaled GEMM)" if args.workload == "train_moe" else
                                "weight quantization (all weights) + per shape: activation quantization, FP8 GEMM"),
                       "timing": "eager" if graph is None else "hip graph replay per step",
                       "device_ms_per_step": round(gpu_ms_per_step, 4),
