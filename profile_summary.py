@@ -33,7 +33,7 @@ def short_name(name):
         bn, bm, wn, wm, _, lay = (int(v) for v in m.groups())
         waves = (bn // wn) * (bm // wm)
         return f"gemm_fp8_kernel {bn}x{bm}/{waves}waves (layout {lay})"
-    m = re.search(r"dg::(quant_\w+)", name)
+    m = re.search(r"dg::(\w+_kernel)", name)
     if m:
         return m.group(1)
     return name[:70]
@@ -43,8 +43,9 @@ def gemm_config(name):
     m = re.search(r"gemm_fp8_kernel<dg::Cfg<(\d+), (\d+), (\d+), (\d+), (\d+)>, (\d)>", name)
     if not m:
         return None
-    bn, bm, wn, wm, _, _ = (int(v) for v in m.groups())
-    return f"gemm_fp8_kernel {bn}x{bm}/{(bn // wn) * (bm // wm)}waves"
+    bn, bm, wn, wm, _, layout = (int(v) for v in m.groups())
+    # layout 3 (per-row B scales) is labelled like bench.py's configuration of the row-scaled GEMM
+    return f"gemm_fp8_kernel {'rowscaled ' if layout == 3 else ''}{bn}x{bm}/{(bn // wn) * (bm // wm)}waves"
 
 
 def cmd_trace(args):
