@@ -24,7 +24,9 @@
 //    global memory into LDS (buffer_load_dwordx4 ... lds: a 32-bit per-lane offset,
 //    the K-block offset in an SGPR, no staging registers) in a
 //    ring of STAGES buffers, each its own __shared__ object so that the compiler's
-//    wait insertion can tell them apart.  Row r's 16-byte chunk c lives at slot
+//    wait insertion can tell them apart.  On the 8-wave tiles one wave per SIMD issues
+//    a stage's DMAs (it stalls while the DMA path drains them) and its SIMD partner
+//    starts its MFMAs meanwhile.  Row r's 16-byte chunk c lives at slot
 //    c ^ f(r), f(r) = (r & 7) ^ ((r >> 3) & 1): the 8 lanes of a DMA that fill one
 //    row write one contiguous 128-byte line, and a fragment read (16 consecutive
 //    rows, one logical chunk) touches 16 distinct 16-byte bank groups.
@@ -56,7 +58,7 @@ __device__ __forceinline__ void lds_dma4(__amdgpu_buffer_rsrc_t rsrc, void* lds,
 template <int V>
 using IC = std::integral_constant<int, V>;
 
-template <int BN_, int BM_, int WN_, int WM_, int STAGES_>
+template <int BN_, int BM_, int WN_, int WM_, int STAGES_, bool HALF_ISSUE_ = false>
 struct Cfg {
   static constexpr int BN = BN_, BM = BM_, WN = WN_, WM = WM_, STAGES = STAGES_;
   static constexpr int kWavesN = BN / WN;
@@ -68,31 +70,39 @@ struct Cfg {
   static constexpr int kSaOffset = (BN + BM) * kGroup;         // BM activation scales follow the tiles
   static constexpr int kSbOffset = kSaOffset + BM * 4;          // then the weight scales (adjacent)
   static constexpr int kSbCount = (BN + 127) / 128;             // 128-row weight blocks of a tile
-  static constexpr int kSbWaveBytes = 16 * ((kSbCount * 4 + 15) / 16);   // one copy per wave
-  static constexpr int kStageBytes = kSbOffset + kWaves * kSbWaveBytes;
-  // per-row B scales (kDenseRowB): BN floats = BN/4 16-byte chunks, spread over the waves' lanes
-  static constexpr int kSbRowLanesPerWave = (BN / 4 + kWaves - 1) / kWaves;
+  static constexpr int kSbWaveBytes = 16 * ((kSbCount * 4 + 15) / 16);   // one copy per issuing wave
+  // Waves that issue the stage DMAs: all of them, or (half issue) the upper half, one wave per
+  // SIMD.  An issuing wave stalls until the DMA path takes its instructions (~64 B/clk/CU); with
+  // half issue the other wave on its SIMD starts its MFMAs meanwhile.
+  static constexpr int kIssuers = HALF_ISSUE_ ? kWaves / 2 : kWaves;
+  // per-row B scales (kDenseRowB): BN floats = BN/4 16-byte chunks, spread over the issuers' lanes
+  static constexpr int kSbRowLanesPerWave = (BN / 4 + kIssuers - 1) / kIssuers;
   static constexpr int kDmaRows = 8;                          // one DMA instruction = 8 rows x 128 B
   static constexpr int kDmaB = BN / kDmaRows;                 // DMA instructions per stage, weights
   static constexpr int kDma = (BN + BM) / kDmaRows;           // ... weights + activations
-  static constexpr int kDmaPerWave = kDma / kWaves;
-  // activation scales: BM floats = BM/4 16-byte chunks, spread over the waves' lanes
-  static constexpr int kSaLanesPerWave = (BM / 4 + kWaves - 1) / kWaves;
-  // vector-memory instructions one thread issues per stage: operand DMAs + the two scale DMAs
+  static constexpr int kDmaPerWave = kDma / kIssuers;         // per issuing wave
+  // activation scales: BM floats = BM/4 16-byte chunks, spread over the issuers' lanes
+  static constexpr int kSaLanesPerWave = (BM / 4 + kIssuers - 1) / kIssuers;
+  // vector-memory instructions an issuing thread issues per stage: operand DMAs + the two scale DMAs
   static constexpr int kVmPerStage = kDmaPerWave + 2;
-  static_assert(kDma % kWaves == 0 && kDmaB % kWaves == 0, "DMA instructions must split evenly over waves");
+  static_assert(kDma % kIssuers == 0 && kDmaB % kIssuers == 0, "DMA instructions must split evenly over waves");
+  static_assert(kIssuers % 2 == 0, "a DMA band must span a multiple of 16 rows (the swizzle period)");
   static_assert(WN % 16 == 0 && WM % 16 == 0 && 128 % WN == 0, "wave tile must be 16-aligned, WN | 128");
   static_assert(STAGES >= 2 && STAGES <= 4, "2..4 stages");
   static_assert(kVmPerStage * (STAGES - 1) < 64, "vmcnt range");
-  static_assert(kSaLanesPerWave <= 64 && BM % 4 == 0, "scale DMA shape");
-  static_assert(kSbRowLanesPerWave <= 64 && BN % 4 == 0, "row-scale DMA shape");
+  // every issuing wave issues exactly kVmPerStage instructions per stage (lane 0 of each scale DMA
+  // is active), which the vmcnt waits count on
+  static_assert(kSaLanesPerWave <= 64 && BM % 4 == 0 && (kIssuers - 1) * kSaLanesPerWave < BM / 4,
+                "scale DMA shape");
+  static_assert(kSbRowLanesPerWave <= 64 && BN % 4 == 0 && (kIssuers - 1) * kSbRowLanesPerWave < BN / 4,
+                "row-scale DMA shape");
 };
 
 // Bytes of one LDS stage: the operand tiles, the activation scales, then the B scales (per-wave
 // copies of the tile's block scales, or BN per-row scales for kDenseRowB).
 template <class C, int LAYOUT>
 constexpr int stage_bytes() {
-  return C::kSbOffset + (LAYOUT == kDenseRowB ? C::BN * 4 : C::kWaves * C::kSbWaveBytes);
+  return C::kSbOffset + (LAYOUT == kDenseRowB ? C::BN * 4 : C::kIssuers * C::kSbWaveBytes);
 }
 
 // LDS slot of 16-byte chunk c of tile row r.  f depends on r mod 16 only, so every fragment
@@ -225,9 +235,11 @@ __global__ __launch_bounds__(C::kThreads) void gemm_fp8_kernel(GemmParams p) {
     // row 8q + i/8, slot i%8), so it loads logical chunk (i%8) ^ f(row).  Each operand has one
     // buffer resource based at the tile's first row and sized to the rows that exist: the hardware
     // range check returns zeros for rows past the N or M edge (those outputs are never stored).
-    constexpr int kBandRows = 8 * C::kWaves;
-    constexpr int kBandsB = C::kDmaB / C::kWaves;
-    const int dma_row = 8 * wave + (lane >> 3);   // tile-local row within band 0 (f(row) is band-invariant)
+    constexpr int kBandRows = 8 * C::kIssuers;
+    constexpr int kBandsB = C::kDmaB / C::kIssuers;
+    const int iw = wave - (C::kWaves - C::kIssuers);   // index among the issuing waves (< 0: not one)
+    const bool issuer = iw >= 0;                      // wave-uniform
+    const int dma_row = 8 * iw + (lane >> 3);   // tile-local row within band 0 (f(row) is band-invariant)
     const int dma_chunk = ((lane & 7) ^ swz_row(dma_row)) << 4;   // byte offset of this lane's chunk in the K block
     // Operand rows are ld bytes apart: k, except for kDenseRowB on a K slice of wider matrices
     // (the per-expert token ranges of the grouped weight gradient).  A resource ends after the last
@@ -241,8 +253,8 @@ __global__ __launch_bounds__(C::kThreads) void gemm_fp8_kernel(GemmParams p) {
         make_rsrc(a_g + (int64_t)m0 * ld, p.m > m0 ? (int64_t)(p.m - m0 - 1) * ld + p.k : 0);
     // activation scales: lanes [kSaLanesPerWave*wave, +kSaLanesPerWave) of the BM/4 16-byte chunks
     // of sa[kb][m0 .. m0+BM); chunks are clamped to the caller's ld_sa row (rows >= m are never stored)
-    const int sa_lane = wave * C::kSaLanesPerWave + lane;
-    const bool sa_active = lane < C::kSaLanesPerWave && sa_lane < C::BM / 4;
+    const int sa_lane = iw * C::kSaLanesPerWave + lane;
+    const bool sa_active = issuer && lane < C::kSaLanesPerWave && sa_lane < C::BM / 4;
     int sa_src_row = m0 + 4 * sa_lane;
     sa_src_row = sa_src_row + 4 <= p.ld_sa ? sa_src_row : (int)p.ld_sa - 4;
     const uint32_t sa_src = (uint32_t)sa_src_row * 4u;   // byte offset within the kb row
@@ -250,8 +262,9 @@ __global__ __launch_bounds__(C::kThreads) void gemm_fp8_kernel(GemmParams p) {
     // n0/128 + i into the wave's own copy (keeps the per-wave vmcnt accounting uniform).  Per-row
     // scales (kDenseRowB): as the activation scales, lanes of every wave fetch the BN/4 16-byte
     // chunks of sb[kb][n0 .. n0+BN), clamped to the caller's ld_sb row.
-    const int sbr_lane = wave * C::kSbRowLanesPerWave + lane;
-    const bool sb_active = kRowB ? (lane < C::kSbRowLanesPerWave && sbr_lane < C::BN / 4) : lane < C::kSbCount;
+    const int sbr_lane = iw * C::kSbRowLanesPerWave + lane;
+    const bool sb_active =
+        issuer && (kRowB ? (lane < C::kSbRowLanesPerWave && sbr_lane < C::BN / 4) : lane < C::kSbCount);
     int sb_blk = (n0 >> 7) + lane;
     sb_blk = sb_blk < p.nb128 ? sb_blk : p.nb128 - 1;
     int sbr_row = n0 + 4 * sbr_lane;
@@ -273,6 +286,7 @@ __global__ __launch_bounds__(C::kThreads) void gemm_fp8_kernel(GemmParams p) {
     // counts kVmPerStage per group).
     auto issue = [&](int tk, auto slot_c) {
       constexpr int slot = decltype(slot_c)::value;
+      if (!issuer) return;
       const int kb = kb_begin + tk;
       uint8_t* sbase = slot == 0 ? st0 : slot == 1 ? st1 : slot == 2 ? st2 : st3;
       // the per-band offsets are recomputed at every issue (one add each) from an opaque copy
@@ -285,19 +299,19 @@ __global__ __launch_bounds__(C::kThreads) void gemm_fp8_kernel(GemmParams p) {
       const bool chunk_out = tail && kb * kGroup + dma_chunk >= p.k;
 #pragma unroll
       for (int u = 0; u < C::kDmaPerWave; ++u) {
-        const int q = wave + C::kWaves * u;
+        const int q = iw + C::kIssuers * u;
         const bool is_b = u < kBandsB;
         const uint32_t voff = base_off + (uint32_t)(is_b ? u : u - kBandsB) * band_step;
         lds_dma16(is_b ? rs_b : rs_a, sbase + q * (C::kDmaRows * kGroup), chunk_out ? 0xFFFFFFF0u : voff,
                   kb * kGroup);
       }
       if (sa_active)
-        lds_dma16(rs_sa, sbase + C::kSaOffset + 16 * wave * C::kSaLanesPerWave, sa_src, kb * (int)p.ld_sa * 4);
+        lds_dma16(rs_sa, sbase + C::kSaOffset + 16 * iw * C::kSaLanesPerWave, sa_src, kb * (int)p.ld_sa * 4);
       if (sb_active) {
         if constexpr (kRowB)
-          lds_dma16(rs_sb, sbase + C::kSbOffset + 16 * wave * C::kSbRowLanesPerWave, sb_src, kb * (int)p.ld_sb * 4);
+          lds_dma16(rs_sb, sbase + C::kSbOffset + 16 * iw * C::kSbRowLanesPerWave, sb_src, kb * (int)p.ld_sb * 4);
         else
-          lds_dma4(rs_sb, sbase + C::kSbOffset + wave * C::kSbWaveBytes, sb_src, kb * 4);
+          lds_dma4(rs_sb, sbase + C::kSbOffset + iw * C::kSbWaveBytes, sb_src, kb * 4);
       }
     };
     auto issue_rt = [&](int tk, int slot) {
@@ -343,7 +357,7 @@ __global__ __launch_bounds__(C::kThreads) void gemm_fp8_kernel(GemmParams p) {
         for (int i = 0; i < C::kFragN; ++i)
           sbr[i] = *reinterpret_cast<const v4f*>(sbase + C::kSbOffset + 4 * (wn0 + 16 * i + 4 * g4));
       } else {
-        const float sbv = sa_l[C::BM + wave * (C::kSbWaveBytes / 4) + sb_idx];   // this wave's copy
+        const float sbv = sa_l[C::BM + (wave % C::kIssuers) * (C::kSbWaveBytes / 4) + sb_idx];   // an issuer's copy
 #pragma unroll
         for (int j = 0; j < C::kFragM; ++j) scale[j] = sa_l[wm0 + 16 * j + l16] * sbv;   // fl32(sa * sb)
       }
@@ -508,9 +522,9 @@ static LaunchInfo info() {
 //              on all twelve M = 64 / 128 DeepSeek-V3 shapes: the 64-row tile, with K split to
 //              fill the grid, is faster on every one.)
 enum CfgId : int { kCfgLarge = 0, kCfgRows128, kCfgWide, kCfgDec64, kCfgDec128, kNumCfg };
-using CfgLarge = Cfg<256, 128, 64, 64, 3>;
-using CfgRows128 = Cfg<256, 128, 64, 64, 3>;
-using CfgWide = Cfg<256, 192, 128, 48, 2>;
+using CfgLarge = Cfg<256, 128, 64, 64, 3, true>;
+using CfgRows128 = Cfg<256, 128, 64, 64, 3, true>;
+using CfgWide = Cfg<256, 192, 128, 48, 2, true>;
 using CfgDec64 = Cfg<64, 64, 32, 32, 4>;
 using CfgDec128 = Cfg<64, 128, 32, 64, 3>;
 
