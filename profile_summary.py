@@ -25,10 +25,14 @@ from collections import defaultdict
 ROOT = os.path.dirname(os.path.abspath(__file__))
 
 
+# tile configuration of a gemm_fp8_kernel instance: BN, BM, WN, WM, STAGES (then optional flags), layout
+_CFG = re.compile(r"gemm_fp8_kernel<dg::Cfg<(\d+), (\d+), (\d+), (\d+), (\d+)(?:, \w+)*>, (\d)>")
+
+
 def short_name(name):
     """'void dg::gemm_fp8_kernel<dg::Cfg<256, 128, 64, 64, 3>, 0>(dg::GemmParams)' ->
     'gemm_fp8_kernel 256x128/8waves (layout 0)'; other kernels: first 70 characters."""
-    m = re.search(r"gemm_fp8_kernel<dg::Cfg<(\d+), (\d+), (\d+), (\d+), (\d+)>, (\d)>", name)
+    m = _CFG.search(name)
     if m:
         bn, bm, wn, wm, _, lay = (int(v) for v in m.groups())
         waves = (bn // wn) * (bm // wm)
@@ -40,7 +44,7 @@ def short_name(name):
 
 
 def gemm_config(name):
-    m = re.search(r"gemm_fp8_kernel<dg::Cfg<(\d+), (\d+), (\d+), (\d+), (\d+)>, (\d)>", name)
+    m = _CFG.search(name)
     if not m:
         return None
     bn, bm, wn, wm, _, layout = (int(v) for v in m.groups())
