@@ -52,12 +52,19 @@ __global__ __launch_bounds__(kTokThreads) void quant_token_group_kernel(
   uint8_t* dst = q + (int64_t)row * k + kb0 * kGroup;
   float* scl = sa + ((int64_t)g * kbc + kb0) * ld_sa + r;
 
-  // lane columns past k (partial last group) read as zeros: the amax is that of the elements present
+  // lane columns past k (partial last group) read as zeros: the amax is that of the elements present.
+  // Every lane loads (an absent column from the row's first element, which exists), so no load
+  // sits behind a branch and all kTokKb of them are in flight together.
   v4f v[kTokKb];
+  bool ok[kTokKb];
+#pragma unroll
+  for (int u = 0; u < kTokKb; ++u) {
+    ok[u] = kb0 + u < kbc && (kb0 + u) * kGroup + 4 * lane < k;
+    v[u] = load4(ok[u] ? src + u * kGroup + 4 * lane : src);
+  }
 #pragma unroll
   for (int u = 0; u < kTokKb; ++u)
-    v[u] = (kb0 + u < kbc && (kb0 + u) * kGroup + 4 * lane < k) ? load4(src + u * kGroup + 4 * lane)
-                                                                : v4f{0.f, 0.f, 0.f, 0.f};
+    if (!ok[u]) v[u] = v4f{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int u = 0; u < kTokKb; ++u) {
     if (kb0 + u >= kbc) break;   // uniform
@@ -81,13 +88,15 @@ constexpr int kBlkThreads = 256;
 __global__ __launch_bounds__(kBlkThreads) void quant_block_kernel(
     const float* __restrict__ w, int64_t n, int64_t k, uint8_t* __restrict__ q,
     float* __restrict__ sb, int64_t nb_n) {
-  const int64_t kbc = (k + kGroup - 1) / kGroup;
-  const int64_t bid = blockIdx.x;
-  const int64_t kb = bid % kbc;
-  const int64_t t = bid / kbc;
-  const int64_t nb = t % nb_n;
-  const int64_t g = t / nb_n;
-  const int64_t row0 = nb * kGroup;
+  // block index -> (matrix, 128-row block, K block) in 32-bit arithmetic (the launcher keeps the
+  // block count, the K-block count and the row-block count below 2^31)
+  const uint32_t kbc = (uint32_t)((k + kGroup - 1) / kGroup);
+  const uint32_t bid = blockIdx.x;
+  const uint32_t kb = bid % kbc;
+  const uint32_t t = bid / kbc;
+  const uint32_t nb = t % (uint32_t)nb_n;
+  const int64_t g = t / (uint32_t)nb_n;
+  const int64_t row0 = (int64_t)nb * kGroup;
   const int rows_here = (int)((n - row0) < kGroup ? (n - row0) : kGroup);
 
   const int tid = threadIdx.x;
@@ -97,15 +106,20 @@ __global__ __launch_bounds__(kBlkThreads) void quant_block_kernel(
   const float* src = w + (g * n + row0) * k + kb * kGroup;
   uint8_t* dst = q + (g * n + row0) * k + kb * kGroup;
 
+  // Every lane loads all 16 of its rows (an absent row or column from the block's first element,
+  // which exists), so no load sits behind a branch and all 16 are in flight together; absent
+  // values are zeroed before the maximum.
   v4f v[16];
-  float amax = 0.0f;
 #pragma unroll
   for (int u = 0; u < 16; ++u) {
     const int r = r0 + 8 * u;
-    if (r < rows_here && col_ok) {
-      v[u] = __builtin_nontemporal_load(reinterpret_cast<const v4f*>(src + r * k) + c4);
-      amax = fmaxf(amax, fmaxf(fmaxf(fabsf(v[u].x), fabsf(v[u].y)), fmaxf(fabsf(v[u].z), fabsf(v[u].w))));
-    }
+    v[u] = __builtin_nontemporal_load(reinterpret_cast<const v4f*>(r < rows_here && col_ok ? src + (int64_t)r * k + 4 * c4 : src));
+  }
+  float amax = 0.0f;
+#pragma unroll
+  for (int u = 0; u < 16; ++u) {
+    if (!(r0 + 8 * u < rows_here && col_ok)) v[u] = v4f{0.f, 0.f, 0.f, 0.f};
+    amax = fmaxf(amax, fmaxf(fmaxf(fabsf(v[u].x), fabsf(v[u].y)), fmaxf(fabsf(v[u].z), fabsf(v[u].w))));
   }
   amax = wave_max(amax);
   __shared__ float red[kBlkThreads / 64];
@@ -118,12 +132,12 @@ __global__ __launch_bounds__(kBlkThreads) void quant_block_kernel(
   for (int u = 0; u < 16; ++u) {
     const int r = r0 + 8 * u;
     if (r < rows_here && col_ok) {
-      reinterpret_cast<uint32_t*>(dst + r * k)[c4] =
+      reinterpret_cast<uint32_t*>(dst + (int64_t)r * k)[c4] =
           pack4_e4m3(clamp448(v[u].x / s), clamp448(v[u].y / s), clamp448(v[u].z / s),
                      clamp448(v[u].w / s));
     }
   }
-  if (tid == 0) sb[(g * nb_n + nb) * kbc + kb] = s;
+  if (tid == 0) sb[(g * nb_n + nb) * (int64_t)kbc + kb] = s;
 }
 
 // ---------------------------------------------------------------------------
@@ -156,11 +170,16 @@ __global__ __launch_bounds__(kChThreads) void quant_channel_group_kernel(
   const T* src = x + ((int64_t)mat * m + tok0 + 8 * oct) * k + col;
 
   // tokens past m (a partial last group) read as zeros: the maxima are those of the tokens present
+  // (every lane loads all 8 tokens - an absent one from the matrix's first element - so that no load
+  // sits behind a branch; absent values are zeroed afterwards)
+  const T* first = x + (int64_t)mat * m * k;
   v4f v[8];
+#pragma unroll
+  for (int u = 0; u < 8; ++u) v[u] = load4(col_ok && tok0 + 8 * oct + u < m ? src + (int64_t)u * k : first);
   v4f amax = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int u = 0; u < 8; ++u) {
-    v[u] = (col_ok && tok0 + 8 * oct + u < m) ? load4(src + (int64_t)u * k) : v4f{0.f, 0.f, 0.f, 0.f};
+    if (!(col_ok && tok0 + 8 * oct + u < m)) v[u] = v4f{0.f, 0.f, 0.f, 0.f};
     amax = v4f{fmaxf(amax.x, fabsf(v[u].x)), fmaxf(amax.y, fabsf(v[u].y)), fmaxf(amax.z, fabsf(v[u].z)),
                fmaxf(amax.w, fabsf(v[u].w))};
   }
