@@ -468,6 +468,43 @@ __global__ __launch_bounds__(C::kThreads) void gemm_fp8_kernel(GemmParams p) {
 
     // ---- epilogue: fp32 -> bf16 (RNE), row-major store, edge masking ------------
     uint16_t* d_g = p.d + (LAYOUT == kMasked ? (int64_t)t.g * p.d_gstride : 0);
+    if ((p.n & 7) == 0) {
+      // Through LDS: a lane's fragment values are 16 rows x 8 bytes apart, so storing them as they
+      // are makes every store instruction touch 16 rows (measured 4.0 TB/s for a bf16 output,
+      // against 6.5 TB/s for row-contiguous 16-byte stores).  Each wave writes one 16-row strip of
+      // its tile (WN columns) into its own padded LDS area of the first ring buffer, reads it back
+      // as 16-byte chunks, and stores whole row segments of WN * 2 bytes.  N % 8 == 0 keeps every
+      // chunk 16-byte aligned and either inside or outside the N edge.
+      constexpr int kPitch = C::WN * 2 + 16;           // padded strip row (bytes)
+      constexpr int kChunksRow = C::WN / 8;            // 16-byte chunks per strip row
+      constexpr int kChunksLane = 16 * kChunksRow / 64;
+      static_assert(kChunksLane * 64 == 16 * kChunksRow, "a strip is a whole number of chunks per lane");
+      static_assert(C::kWaves * 16 * kPitch <= kStage, "the strips fit in one ring buffer");
+      uint8_t* strip = st0 + wave * (16 * kPitch);
+      __syncthreads();   // every wave is done with the ring (the last K block's operands)
+#pragma unroll
+      for (int j = 0; j < C::kFragM; ++j) {
+#pragma unroll
+        for (int i = 0; i < C::kFragN; ++i) {
+          uint2 v;
+          v.x = (uint32_t)f32_to_bf16_rne(acc[i][j][0]) | ((uint32_t)f32_to_bf16_rne(acc[i][j][1]) << 16);
+          v.y = (uint32_t)f32_to_bf16_rne(acc[i][j][2]) | ((uint32_t)f32_to_bf16_rne(acc[i][j][3]) << 16);
+          *reinterpret_cast<uint2*>(strip + l16 * kPitch + (16 * i + 4 * g4) * 2) = v;
+        }
+        // the wave reads back what its own lanes wrote (LDS operations of one wave complete in order)
+#pragma unroll
+        for (int u = 0; u < kChunksLane; ++u) {
+          const int c = lane + 64 * u;
+          const int row = c / kChunksRow, cc = c % kChunksRow;
+          const u32x4 val = *reinterpret_cast<const u32x4*>(strip + row * kPitch + cc * 16);
+          const int mrow = m0 + wm0 + 16 * j + row;
+          const int ncol = n0 + wn0 + 8 * cc;
+          if (mrow < t.m_valid && ncol < p.n)
+            *reinterpret_cast<u32x4*>(d_g + (int64_t)mrow * p.n + ncol) = val;
+        }
+      }
+      continue;
+    }
     const bool vec_ok = (p.n & 3) == 0;
 #pragma unroll
     for (int j = 0; j < C::kFragM; ++j) {
