@@ -136,7 +136,7 @@ __device__ __forceinline__ void wait_groups(int younger) {
 }
 
 struct TileCoord {
-  int g, mb, nbt, split, m_valid, tile_id;
+  int g, mb, nbt, split, m_valid;
 };
 
 template <class C, int LAYOUT>
@@ -171,8 +171,11 @@ __global__ __launch_bounds__(C::kThreads) void gemm_fp8_kernel(GemmParams p) {
     masked_item_prefix(p.masked_m, p.num_groups, p.m, C::BM, p.tiles_n, s_prefix, s_scan);
     total_items = s_prefix[p.num_groups] * p.splits;
   } else {
-    // contiguous: the expert comes from m_indices, not from the item index
-    total_items = p.tiles_m * p.tiles_n * (LAYOUT == kDense ? p.num_groups : 1) * p.splits;
+    // contiguous: the expert comes from m_indices, not from the item index.  The first tail_start
+    // tiles are whole work items, each later tile is `splits` items (a K split that fills the last,
+    // partial round of the persistent grid)
+    const int tiles = p.tiles_m * p.tiles_n * (LAYOUT == kDense ? p.num_groups : 1);
+    total_items = p.tail_start + (tiles - p.tail_start) * p.splits;
   }
 
   // XCD-aware order: workgroup b runs on XCD b % 8; give each XCD a contiguous
@@ -184,8 +187,11 @@ __global__ __launch_bounds__(C::kThreads) void gemm_fp8_kernel(GemmParams p) {
   for (int item = wg; item < total_items; item += grid) {
     // ---- decode the item ------------------------------------------------------
     TileCoord t;
-    t.split = item % p.splits;
-    int rest = item / p.splits;
+    // whole tile (item < tail_start) or split `t.split` of split tile `sidx`
+    const bool split_item = item >= p.tail_start;
+    const int sidx = (item - p.tail_start) / p.splits;
+    t.split = split_item ? (item - p.tail_start) % p.splits : 0;
+    int rest = split_item ? p.tail_start + sidx : item;
     if constexpr (LAYOUT == kMasked) {
       const int g = masked_group_of(s_prefix, p.num_groups, rest);
       rest -= s_prefix[g];
@@ -195,7 +201,6 @@ __global__ __launch_bounds__(C::kThreads) void gemm_fp8_kernel(GemmParams p) {
       t.nbt = rest / mblocks;
       int mv = p.masked_m[g];
       t.m_valid = mv < 0 ? 0 : (mv > p.m ? p.m : mv);
-      t.tile_id = (g * p.tiles_m + t.mb) * p.tiles_n + t.nbt;
     } else {
       // grouped order: runs of kGroupM m-tiles x all n-tiles, m fastest inside a run, so the
       // grid/8 consecutive items one XCD takes per round cover ~8 activation panels and a few
@@ -211,7 +216,6 @@ __global__ __launch_bounds__(C::kThreads) void gemm_fp8_kernel(GemmParams p) {
       t.mb = first_m + in_run % run_m;
       t.nbt = in_run / run_m;
       t.m_valid = p.m;
-      t.tile_id = (t.g * p.tiles_m + t.mb) * p.tiles_n + t.nbt;
     }
     const int m0 = t.mb * C::BM;
     const int n0 = t.nbt * C::BN;
@@ -220,8 +224,8 @@ __global__ __launch_bounds__(C::kThreads) void gemm_fp8_kernel(GemmParams p) {
       expert = p.m_indices[m0];
       if (expert < 0 || expert >= p.num_groups) continue;   // uniform: skip unmapped block
     }
-    const int kb_begin = t.split * p.kb_per_split;
-    int kb_end = kb_begin + p.kb_per_split;
+    const int kb_begin = split_item ? t.split * p.kb_per_split : 0;
+    int kb_end = split_item ? kb_begin + p.kb_per_split : p.kb_total;
     if (kb_end > p.kb_total) kb_end = p.kb_total;
     const int nk = kb_end - kb_begin;
 
@@ -420,11 +424,11 @@ __global__ __launch_bounds__(C::kThreads) void gemm_fp8_kernel(GemmParams p) {
     // write through the XCD's L2, completion is awaited with s_waitcnt before the
     // arrival counter is bumped, and the last workgroup reads them back with
     // agent-scope loads, which miss in its own (non-coherent) L2.
-    if (p.splits > 1) {
+    if (split_item && p.splits > 1) {
       // partial layout: [fragment][thread][4] - 16 bytes per thread and fragment (coalesced)
       constexpr int kFrags = C::kFragN * C::kFragM;
       constexpr int kSplitBytes = kFrags * NT * 16;
-      float* ws_tile = p.ws + (int64_t)t.tile_id * p.splits * (int64_t)(kSplitBytes / 4);
+      float* ws_tile = p.ws + (int64_t)sidx * p.splits * (int64_t)(kSplitBytes / 4);
       const __amdgpu_buffer_rsrc_t rs_ws = make_rsrc(ws_tile, (int64_t)p.splits * kSplitBytes);
       const int own = t.split * kSplitBytes + tid * 16;
 #pragma unroll
@@ -435,7 +439,7 @@ __global__ __launch_bounds__(C::kThreads) void gemm_fp8_kernel(GemmParams p) {
       __syncthreads();
       if (tid == 0) {
         const unsigned prev =
-            __hip_atomic_fetch_add(p.counters + t.tile_id, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            __hip_atomic_fetch_add(p.counters + sidx, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         s_flag = (prev == (unsigned)(p.splits - 1)) ? 1 : 0;
       }
       __syncthreads();
@@ -463,7 +467,7 @@ __global__ __launch_bounds__(C::kThreads) void gemm_fp8_kernel(GemmParams p) {
         }
       }
       if (tid == 0)   // leave the counter zeroed for the next call
-        __hip_atomic_store(p.counters + t.tile_id, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(p.counters + sidx, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
 
     // ---- epilogue: fp32 -> bf16 (RNE), row-major store, edge masking ------------
@@ -590,10 +594,11 @@ static int occupancy(const LaunchInfo& li) {
 struct Plan {
   int cfg;
   int bn, bm;
-  int splits;
+  int splits;        // K splits of each split tile
   int kb_per_split;
+  int tail_start;    // tiles [0, tail_start) run whole; the rest are split (0: every tile)
   int tiles_m, tiles_n;
-  int64_t tiles;     // output tiles (one split-K counter each)
+  int64_t tiles;     // output tiles
   size_t ws_bytes;   // needed workspace for this plan (0 when splits == 1)
 };
 
@@ -604,12 +609,17 @@ static void finish_plan(Plan& pl, int64_t m, int64_t n, int64_t k, int64_t group
   pl.tiles_m = (int)((m + li.bm - 1) / li.bm);
   pl.tiles_n = (int)((n + li.bn - 1) / li.bn);
   pl.tiles = (int64_t)pl.tiles_m * pl.tiles_n * groups;
-  if (pl.tiles > kMaxCounterTiles) {   // one arrival counter per tile must fit the counter prefix
+  if (pl.tail_start > pl.tiles) pl.tail_start = 0;
+  const int64_t split_tiles = pl.tiles - pl.tail_start;
+  if (split_tiles > kMaxCounterTiles) {   // one arrival counter per split tile must fit the counter prefix
     pl.splits = 1;
+    pl.tail_start = 0;
     pl.kb_per_split = (int)((k + kGroup - 1) / kGroup);
   }
+  if (pl.splits == 1) pl.tail_start = 0;
   pl.ws_bytes = 0;
-  if (pl.splits > 1) pl.ws_bytes = kCounterBytes + (size_t)pl.tiles * pl.splits * (size_t)li.bn * li.bm * 4;
+  if (pl.splits > 1)
+    pl.ws_bytes = kCounterBytes + (size_t)(pl.tiles - pl.tail_start) * pl.splits * (size_t)li.bn * li.bm * 4;
 }
 
 // Large-m tile choice: estimated time = rounds of the persistent grid x time per tile round.  A
@@ -655,6 +665,7 @@ static Plan make_decode_plan(int64_t m, int64_t n, int64_t k, int64_t groups, in
   Plan pl{};
   pl.cfg = m <= 64 ? kCfgDec64 : kCfgDec128;
   pl.splits = 1;
+  pl.tail_start = 0;
   pl.kb_per_split = kb_total;
   const LaunchInfo li = cfg_info<kDense>(pl.cfg);
   const int occ = occupancy(li);
@@ -684,14 +695,32 @@ static Plan make_plan(int layout, int64_t m, int64_t n, int64_t k, int64_t group
   const LaunchInfo li = cfg_info<kDense>(pl.cfg);
   const int kb_total = (int)((k + kGroup - 1) / kGroup);
   pl.splits = 1;
+  pl.tail_start = 0;
   // few tiles and a long K (e.g. 256 x 512 x 8192): split K so that every CU gets work
   const int64_t tiles = ((m + li.bm - 1) / li.bm) * ((n + li.bn - 1) / li.bn) * groups;
+  const int max_split = kb_total / 4 > 0 ? kb_total / 4 : 1;   // keep >= 4 K blocks per split
+  const int64_t grid = (int64_t)num_cus * occupancy(li);
   if (allow_split && 2 * tiles <= num_cus) {
     int want = (int)(num_cus / tiles);
-    const int max_split = kb_total / 4 > 0 ? kb_total / 4 : 1;   // keep >= 4 K blocks per split
     if (want > max_split) want = max_split;
     if (want > kMaxSplits) want = kMaxSplits;
     if (want > 1) pl.splits = want;
+  } else if (allow_split && (layout == kDense || layout == kDenseRowB) && tiles > grid && tiles % grid != 0 &&
+             2 * (tiles % grid) <= grid) {
+    // The last round of the persistent grid holds tiles % grid tiles (e.g. 616 tiles of 4096 x 7168
+    // on 256 CUs: two full rounds and 104 tiles).  Those tiles are split in K over the idle
+    // workgroups, so the last round takes 1/splits of a round instead of a whole one.  The split's
+    // hand-off (partials out and back, ~20 us) must cost less than the part of a round it saves:
+    // every piece keeps >= 24 K blocks (measured on MI355X: 4096 x 7168 x 16384 13% faster; with
+    // 4-8 K blocks per piece, K = 1536 and 2048, 3-6% slower).
+    const int64_t tail = tiles % grid;
+    int want = (int)(grid / tail);
+    if (want > kb_total / 24) want = kb_total / 24;
+    if (want > kMaxSplits) want = kMaxSplits;
+    if (want > 1) {
+      pl.splits = want;
+      pl.tail_start = (int)(tiles - tail);
+    }
   }
   pl.kb_per_split = (kb_total + pl.splits - 1) / pl.splits;
   pl.splits = (kb_total + pl.kb_per_split - 1) / pl.kb_per_split;   // no empty split
@@ -703,7 +732,10 @@ void gemm_config_name(int layout, int64_t m, int64_t n, int64_t k, int64_t group
                       size_t len) {
   const Plan pl = make_plan(layout, m, n, k, layout == kMasked ? groups : 1, num_cus, layout != kContiguous);
   const LaunchInfo li = cfg_info<kDense>(pl.cfg);
-  snprintf(buf, len, "%dx%d/%dwaves/split%d", li.bn, li.bm, li.threads / 64, pl.splits);
+  if (pl.tail_start > 0)   // whole tiles, then a split last round
+    snprintf(buf, len, "%dx%d/%dwaves/split1+tail%d", li.bn, li.bm, li.threads / 64, pl.splits);
+  else
+    snprintf(buf, len, "%dx%d/%dwaves/split%d", li.bn, li.bm, li.threads / 64, pl.splits);
 }
 
 size_t gemm_workspace_size(int64_t m, int64_t n, int64_t k, int64_t groups, int num_cus) {
@@ -718,7 +750,8 @@ template <int LAYOUT>
 static int launch_layout(GemmParams p, const Plan& pl, hipStream_t stream, int num_cus) {
   const LaunchInfo li = cfg_info<LAYOUT>(pl.cfg);
   const int occ = occupancy(li);
-  const int64_t items = (int64_t)pl.tiles_m * pl.tiles_n * (LAYOUT == kContiguous ? 1 : p.num_groups) * pl.splits;
+  const int64_t tiles = (int64_t)pl.tiles_m * pl.tiles_n * (LAYOUT == kContiguous ? 1 : p.num_groups);
+  const int64_t items = pl.tail_start + (tiles - pl.tail_start) * pl.splits;
   if (items > 0x7fffffffLL) return set_error(kUnsupported, "gemm: too many work items");
   int64_t grid = (int64_t)num_cus * occ;
   if (grid > items) grid = items;
@@ -754,6 +787,7 @@ int launch_gemm(int layout, const uint8_t* a, const float* sa, int64_t ld_sa, co
   p.nb128 = (int)((n + kGroup - 1) / kGroup);
   p.tiles_m = pl.tiles_m; p.tiles_n = pl.tiles_n;
   p.splits = pl.splits; p.kb_per_split = pl.kb_per_split;
+  p.tail_start = pl.tail_start;
   p.a_gstride = m * k;
   p.sa_gstride = (int64_t)p.kb_total * ld_sa;
   p.b_gstride = n * k;

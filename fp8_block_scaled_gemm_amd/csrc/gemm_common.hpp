@@ -22,7 +22,7 @@ struct GemmParams {
   const int32_t* m_indices;   // contiguous: expert per row
   const int32_t* masked_m;    // masked: valid rows per group
   float* ws;                  // split-K partials
-  unsigned* counters;         // split-K arrival counters, one per output tile
+  unsigned* counters;         // split-K arrival counters, one per split output tile
   int64_t ld_sa;
   int64_t ld_sb;             // kDenseRowB: row stride of the per-row B scales
   int ld_ab;                 // kDenseRowB: row stride (bytes) of both operands (k, or larger for K slices)
@@ -33,8 +33,9 @@ struct GemmParams {
   int kb_total;     // k / 128
   int tiles_m;      // ceil(m / BM)
   int tiles_n;      // ceil(n / BN)
-  int splits;       // K splits (1 = none)
+  int splits;       // K splits of the split tiles (1 = none)
   int kb_per_split;
+  int tail_start;   // work items [0, tail_start) are whole tiles; every later tile is split in `splits`
   int nb128;        // ceil(n / 128): weight-scale rows per group
 };
 

@@ -55,6 +55,24 @@ def test_ragged_shapes(m, n, k):
     check_gemm(run_dense(qa, sa, qb, sb, ld_extra=4), ref, f"ragged {m}x{n}x{k}")
 
 
+@pytest.mark.parametrize("m,n,k", [(4608, 4096, 6144), (4096, 7168, 6144)])
+def test_split_last_round(m, n, k):
+    """More tiles than the persistent grid holds, with a partial last round and a long K: the whole
+    tiles of the full rounds run unsplit and the last round's tiles are split in K (split1+tailN).
+    Against the oracle, bit-identical on a repeat, and within tolerance of the unsplit
+    (no-workspace) plan."""
+    name = dg.dg_gemm_config_name(0, m, n, k)
+    say("gemm split last round", m, n, k, name)
+    if dg.dg_get_num_cus() == 256:   # 256x192 tiles: 22 x 28 = 616 (tail 104), 24 x 16 = 384 (tail 128)
+        assert "+tail" in name, name
+    qa, sa, qb, sb = quantized_operands("tail", m, n, k)
+    ref = oracle.gemm.gemm_nt(qa, sa, qb, sb)
+    d1, d2 = run_dense(qa, sa, qb, sb), run_dense(qa, sa, qb, sb)
+    assert np.array_equal(bf16_bits(d1), bf16_bits(d2))
+    check_gemm(d1, ref, f"split last round {m}x{n}x{k}")
+    check_gemm(run_dense(qa, sa, qb, sb, workspace=False), ref, f"unsplit {m}x{n}x{k}")
+
+
 def test_split_k_deterministic():
     """Small M with a long K takes the split-K path; repeated calls are bit-identical and the
     no-workspace path agrees within tolerance."""

@@ -103,7 +103,8 @@ def run_row_scaled(qa, sa, qb, sb, ld_extra=0, workspace=True):
 
 
 @pytest.mark.parametrize("m,n,k", [(256, 256, 256), (200, 130, 384), (4096, 512, 1024), (64, 7168, 2048),
-                                   (128, 4096, 7168), (300, 520, 272), (1, 16, 128), (1000, 2000, 1536)])
+                                   (128, 4096, 7168), (300, 520, 272), (1, 16, 128), (1000, 2000, 1536),
+                                   (2048, 5120, 1024)])
 def test_row_scaled_gemm(m, n, k):
     say("row-scaled gemm", m, n, k, dg.dg_gemm_config_name(3, m, n, k))
     qa, sa, qb, sb = row_scaled_operands("rowscaled", m, n, k)
