@@ -558,10 +558,11 @@ static LaunchInfo info() {
 //  kCfgWide    256x192, 8 waves of 128x48, 2 stages (~114 KB LDS): 1.5x the work per tile and
 //              ~1/6 less operand traffic per flop than kCfgLarge; chosen when it needs fewer
 //              rounds of the persistent grid (wave quantisation decides most shapes).
-//  kCfgDec*    m <= 64 / m <= 128 rows: 64 weight rows x 64 or 128 activation rows, 4 waves,
-//              two workgroups per CU: HBM-bound shapes.  (Measured against 128-row weight tiles
-//              on all twelve M = 64 / 128 DeepSeek-V3 shapes: the 64-row tile, with K split to
-//              fill the grid, is faster on every one.)
+//  kCfgDec*    m <= 128 rows: 64 weight rows x 64 or 128 activation rows, 4 waves, two
+//              workgroups per CU: HBM-bound shapes (for 65..128 rows the planner's model picks
+//              one 128-row or two 64-row activation tiles).  (Measured against 128-row weight
+//              tiles on all twelve M = 64 / 128 DeepSeek-V3 shapes: the 64-row weight tile, with
+//              K split to fill the grid, is faster on every one.)
 enum CfgId : int { kCfgLarge = 0, kCfgRows128, kCfgWide, kCfgDec64, kCfgDec128, kNumCfg };
 using CfgLarge = Cfg<256, 128, 64, 64, 3, true>;
 using CfgRows128 = Cfg<256, 128, 64, 64, 3, true>;
@@ -667,20 +668,27 @@ static Plan make_decode_plan(int64_t m, int64_t n, int64_t k, int64_t groups, in
   pl.splits = 1;
   pl.tail_start = 0;
   pl.kb_per_split = kb_total;
-  const LaunchInfo li = cfg_info<kDense>(pl.cfg);
-  const int occ = occupancy(li);
   int max_split = kb_total / 2 < kMaxSplits ? kb_total / 2 : kMaxSplits;
   if (!allow_split || max_split < 1) max_split = 1;
+  // 65..128 rows: either one 128-row activation tile or two 64-row ones, whichever the model rates
+  // faster (the 64-row tile moves less per K block and wins where the split count matters, e.g.
+  // 128 x 7168 x 2048 unsplit on 64-row tiles: 9.8 us against 11.9 us on 128-row tiles, split 2)
+  const int cfgs[2] = {kCfgDec64, kCfgDec128};
   double best_t = 1e30;
-  for (int want = 1; want <= max_split; ++want) {
-    const int kbps = (kb_total + want - 1) / want;
-    const int splits = (kb_total + kbps - 1) / kbps;
-    if (splits != want) continue;   // the same split as a smaller request
-    const double t = decode_estimate(li, occ, m, n, kb_total, groups, num_cus, splits, kbps);
-    if (t < best_t) {
-      best_t = t;
-      pl.splits = splits;
-      pl.kb_per_split = kbps;
+  for (int c = 0; c < (m <= 64 ? 1 : 2); ++c) {
+    const LaunchInfo li = cfg_info<kDense>(cfgs[c]);
+    const int occ = occupancy(li);
+    for (int want = 1; want <= max_split; ++want) {
+      const int kbps = (kb_total + want - 1) / want;
+      const int splits = (kb_total + kbps - 1) / kbps;
+      if (splits != want) continue;   // the same split as a smaller request
+      const double t = decode_estimate(li, occ, m, n, kb_total, groups, num_cus, splits, kbps);
+      if (t < best_t) {
+        best_t = t;
+        pl.cfg = cfgs[c];
+        pl.splits = splits;
+        pl.kb_per_split = kbps;
+      }
     }
   }
   finish_plan(pl, m, n, k, groups);
