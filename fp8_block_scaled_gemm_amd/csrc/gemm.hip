@@ -491,8 +491,8 @@ __global__ __launch_bounds__(C::kThreads) void gemm_fp8_kernel(GemmParams p) {
 #pragma unroll
         for (int i = 0; i < C::kFragN; ++i) {
           uint2 v;
-          v.x = (uint32_t)f32_to_bf16_rne(acc[i][j][0]) | ((uint32_t)f32_to_bf16_rne(acc[i][j][1]) << 16);
-          v.y = (uint32_t)f32_to_bf16_rne(acc[i][j][2]) | ((uint32_t)f32_to_bf16_rne(acc[i][j][3]) << 16);
+          v.x = pack2_bf16_rne(acc[i][j][0], acc[i][j][1]);
+          v.y = pack2_bf16_rne(acc[i][j][2], acc[i][j][3]);
           *reinterpret_cast<uint2*>(strip + l16 * kPitch + (16 * i + 4 * g4) * 2) = v;
         }
         // the wave reads back what its own lanes wrote (LDS operations of one wave complete in order)
@@ -518,14 +518,13 @@ __global__ __launch_bounds__(C::kThreads) void gemm_fp8_kernel(GemmParams p) {
 #pragma unroll
       for (int i = 0; i < C::kFragN; ++i) {
         const int ncol = n0 + wn0 + 16 * i + 4 * g4;
-        const uint16_t h0 = f32_to_bf16_rne(acc[i][j][0]);
-        const uint16_t h1 = f32_to_bf16_rne(acc[i][j][1]);
-        const uint16_t h2 = f32_to_bf16_rne(acc[i][j][2]);
-        const uint16_t h3 = f32_to_bf16_rne(acc[i][j][3]);
+        const uint32_t lo = pack2_bf16_rne(acc[i][j][0], acc[i][j][1]);
+        const uint32_t hi = pack2_bf16_rne(acc[i][j][2], acc[i][j][3]);
+        const uint16_t h0 = (uint16_t)lo, h1 = (uint16_t)(lo >> 16), h2 = (uint16_t)hi, h3 = (uint16_t)(hi >> 16);
         if (vec_ok && ncol + 3 < p.n) {
           uint2 v;
-          v.x = (uint32_t)h0 | ((uint32_t)h1 << 16);
-          v.y = (uint32_t)h2 | ((uint32_t)h3 << 16);
+          v.x = lo;
+          v.y = hi;
           *reinterpret_cast<uint2*>(drow + ncol) = v;
         } else {
           if (ncol + 0 < p.n) drow[ncol + 0] = h0;
