@@ -123,6 +123,55 @@ def test_closed_form_hadamard():
     assert np.array_equal(d, 448.0 * 448.0 * 128 * np.eye(128))
 
 
+def _rounding_cases(count):
+    """fp32 bit patterns for the bf16 rounding test: ties to even in both directions, just below and
+    above ties, large values that round to infinity, subnormals, both signs; then random patterns."""
+    base = []
+    for hi in (0x3F80, 0x3F81, 0x4049, 0x404A, 0x7F7F, 0x7F7E, 0x0001, 0x0040, 0x00FF, 0x0080, 0x3400):
+        for lo in (0x8000, 0x7FFF, 0x8001, 0x0000, 0xFFFF, 0x4000, 0xC000):
+            base.append((hi << 16) | lo)
+    base += [0x7F7FFFFF, 0x7F7F8000, 0x7F7F7FFF, 0x00008000, 0x00018000, 0x00000001, 0x007FFFFF]
+    rng = np.random.default_rng(11)
+    rand = rng.integers(0, 1 << 31, size=count, dtype=np.int64)
+    rand = rand[((rand >> 23) & 0xFF) != 0xFF]   # finite patterns only
+    pos = np.array(base + list(rand), dtype=np.int64)[: count // 2]
+    bits = np.concatenate([pos, pos | (1 << 31)])[:count]   # and the negatives
+    return bits.astype(np.uint32)
+
+
+def test_bf16_output_rounding():
+    """Closed form for the epilogue's fp32 -> bf16 rounding: A and B one-hot (one +-1.0 per row, same K
+    column for row i of A and row i of B, block scales 1), so output (i, i) is exactly the activation
+    scale sa[i] (+-), which is chosen to hit round-to-nearest-even ties, near-ties, overflow and
+    subnormals; every diagonal element must equal torch's CPU bf16 conversion of that fp32 value,
+    every other element is 0."""
+    m = n = 256
+    k = 256
+    say("gemm bf16 rounding", m, n, k, dg.dg_gemm_config_name(0, m, n, k))
+    bits = _rounding_cases(m)
+    vals = bits.view(np.float32)
+    qa = np.zeros((m, k), np.uint8)
+    qb = np.zeros((n, k), np.uint8)
+    idx = np.arange(m)
+    qa[idx, idx % 128] = 0x38            # E4M3 1.0 (the sign goes into the scale)
+    qb[idx, idx % 128] = 0x38
+    sa = np.ones((m, k // 128), np.float32)
+    sa[:, 0] = vals                      # K group 0 holds the only nonzero product of row i
+    sb = np.ones((n // 128, k // 128), np.float32)
+    d = run_dense(qa, sa, qb, sb)
+    got = bf16_bits(d)
+    want = torch.from_numpy(vals.copy()).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    diag = got[idx, idx]
+    bad = np.nonzero(diag != want)[0]
+    assert bad.size == 0, [(hex(int(bits[i])), hex(int(diag[i])), hex(int(want[i]))) for i in bad[:5]]
+    off = got.copy()
+    off[idx, idx] = 0
+    same_col = (idx[:, None] % 128 == idx[None, :] % 128) & (idx[:, None] != idx[None, :])
+    # rows i and i +- 128 share a K column: those entries carry row i's value as well
+    assert np.array_equal(off[same_col], np.broadcast_to(want[:, None], (m, n))[same_col])
+    assert np.all(off[~same_col] == 0)
+
+
 def test_kblock_rebalance_bit_identical():
     """Scaling K block kb of A by 2^j and of B by 2^-j leaves the output bit-identical."""
     say("gemm k-block rebalance")
