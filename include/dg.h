@@ -123,12 +123,15 @@ int dg_quantize_per_block(const float* w, int64_t num_groups, int64_t n, int64_t
  * a  : E4M3 (m, k) row-major.        sa : fp32, MN-major with stride ld_sa (see above).
  * b  : E4M3 (n, k) row-major.        sb : fp32 (ceil(n/128), KB).
  * d  : bf16 (m, n) row-major, written.
- * workspace : optional device scratch for split-K on small-m shapes.  Its first
- *   64 KiB hold per-tile arrival counters: they must be zero before the first
+ * workspace : optional device scratch for K splits: every tile of a small-m shape, or the
+ *   tiles of a large shape's partial last round of the persistent grid (long K only).
+ *   Its first 64 KiB hold per-tile arrival counters: they must be zero before the first
  *   use (e.g. a zero-filled allocation), and every call leaves them zero; the
  *   rest holds fp32 partials.  Calls sharing one workspace must be ordered on
  *   one stream (concurrent calls race).  NULL or too small (see
- *   dg_gemm_workspace_size) => no split-K: still correct, slower for small m.
+ *   dg_gemm_workspace_size) => no split: still correct, slower (the rounding of
+ *   the split tiles' outputs may differ in the last bit: partials are summed in
+ *   fixed split order).
  * Errors: DG_ERR_INVALID_ARG for null/misaligned pointers, negative sizes,
  * k % 16 != 0, ld_sa < m or ld_sa % 4 != 0.  Deterministic: the same inputs
  * give bit-identical outputs.
@@ -277,7 +280,8 @@ int64_t dg_get_scale_ld(int64_t rows);
 size_t dg_gemm_workspace_size(int64_t m, int64_t n, int64_t k, int64_t num_groups);
 
 /* Name of the tile configuration and K split the GEMM picks for a shape, as
- * "BNxBM/WNxWM/splitS" (static thread-local string), assuming a large enough
+ * "BNxBM/Wwaves/splitS", or "BNxBM/Wwaves/split1+tailS" when only the last round's
+ * tiles are split in S (static thread-local string), assuming a large enough
  * workspace.  layout: 0 normal, 1 contiguous-grouped, 2 masked-grouped (m = rows
  * per group), 3 row-scaled normal.  For profiling and reports; returns "" for invalid arguments. */
 const char* dg_gemm_config_name(int layout, int64_t m, int64_t n, int64_t k, int64_t num_groups);
