@@ -622,14 +622,29 @@ static void finish_plan(Plan& pl, int64_t m, int64_t n, int64_t k, int64_t group
     pl.ws_bytes = kCounterBytes + (size_t)(pl.tiles - pl.tail_start) * pl.splits * (size_t)li.bn * li.bm * 4;
 }
 
+// K splits of the tiles in the partial last round of the persistent grid (1: none).  That round
+// holds tiles % grid tiles; split in K over the idle workgroups, it takes 1/splits of a round.  The
+// split's hand-off (partials out and back, ~20 us) must cost less than the part of a round it
+// saves: every piece keeps >= 24 K blocks (measured on MI355X: 4096 x 7168 x 16384 13% faster;
+// with 4-8 K blocks per piece, K = 1536 and 2048, 3-6% slower).
+static int last_round_splits(int64_t tiles, int64_t grid, int kb_total) {
+  if (tiles <= grid || tiles % grid == 0 || 2 * (tiles % grid) > grid) return 1;
+  int want = (int)(grid / (tiles % grid));
+  if (want > kb_total / 24) want = kb_total / 24;
+  if (want > kMaxSplits) want = kMaxSplits;
+  return want > 1 ? want : 1;
+}
+
 // Large-m tile choice: estimated time = rounds of the persistent grid x time per tile round.  A
 // 256x192 tile round takes ~1.22x a 256x128 round (1.5x the MFMA work, less operand traffic per
 // flop; measured on MI355X over nine shapes with M = 2048..16384), so it wins where it saves a
 // round, e.g. 4096x2112 (198 tiles, one round, vs 288) or 4096x7168 (3 rounds vs 3.5).
-static int choose_large(int64_t m, int64_t n, int64_t groups, int num_cus) {
+static int choose_large(int64_t m, int64_t n, int64_t groups, int num_cus, int kb_total, bool split_tail) {
   auto rounds = [&](int bn, int bm) {
     const int64_t tiles = ((m + bm - 1) / bm) * ((n + bn - 1) / bn) * groups;
-    return (tiles + num_cus - 1) / num_cus;   // both configurations run one workgroup per CU
+    // both configurations run one workgroup per CU; a split last round counts 1/splits of a round
+    const int s = split_tail ? last_round_splits(tiles, num_cus, kb_total) : 1;
+    return s > 1 ? (double)(tiles / num_cus) + 1.0 / s : (double)((tiles + num_cus - 1) / num_cus);
   };
   const double t_large = (double)rounds(CfgLarge::BN, CfgLarge::BM);
   const double t_wide = 1.22 * (double)rounds(CfgWide::BN, CfgWide::BM);
@@ -698,9 +713,11 @@ static Plan make_decode_plan(int64_t m, int64_t n, int64_t k, int64_t groups, in
 static Plan make_plan(int layout, int64_t m, int64_t n, int64_t k, int64_t groups, int num_cus, bool allow_split) {
   if (layout != kContiguous && m <= 128) return make_decode_plan(m, n, k, groups, num_cus, allow_split);
   Plan pl{};
-  pl.cfg = layout == kContiguous ? kCfgRows128 : layout == kDenseRowB ? kCfgLarge : choose_large(m, n, groups, num_cus);
-  const LaunchInfo li = cfg_info<kDense>(pl.cfg);
   const int kb_total = (int)((k + kGroup - 1) / kGroup);
+  pl.cfg = layout == kContiguous ? kCfgRows128
+           : layout == kDenseRowB ? kCfgLarge
+                                  : choose_large(m, n, groups, num_cus, kb_total, allow_split && layout == kDense);
+  const LaunchInfo li = cfg_info<kDense>(pl.cfg);
   pl.splits = 1;
   pl.tail_start = 0;
   // few tiles and a long K (e.g. 256 x 512 x 8192): split K so that every CU gets work
@@ -712,21 +729,13 @@ static Plan make_plan(int layout, int64_t m, int64_t n, int64_t k, int64_t group
     if (want > max_split) want = max_split;
     if (want > kMaxSplits) want = kMaxSplits;
     if (want > 1) pl.splits = want;
-  } else if (allow_split && (layout == kDense || layout == kDenseRowB) && tiles > grid && tiles % grid != 0 &&
-             2 * (tiles % grid) <= grid) {
-    // The last round of the persistent grid holds tiles % grid tiles (e.g. 616 tiles of 4096 x 7168
-    // on 256 CUs: two full rounds and 104 tiles).  Those tiles are split in K over the idle
-    // workgroups, so the last round takes 1/splits of a round instead of a whole one.  The split's
-    // hand-off (partials out and back, ~20 us) must cost less than the part of a round it saves:
-    // every piece keeps >= 24 K blocks (measured on MI355X: 4096 x 7168 x 16384 13% faster; with
-    // 4-8 K blocks per piece, K = 1536 and 2048, 3-6% slower).
-    const int64_t tail = tiles % grid;
-    int want = (int)(grid / tail);
-    if (want > kb_total / 24) want = kb_total / 24;
-    if (want > kMaxSplits) want = kMaxSplits;
+  } else if (allow_split && (layout == kDense || layout == kDenseRowB)) {
+    // e.g. 616 tiles of 4096 x 7168 on 256 CUs: two full rounds, and the last round's 104 tiles
+    // split in K
+    const int want = last_round_splits(tiles, grid, kb_total);
     if (want > 1) {
       pl.splits = want;
-      pl.tail_start = (int)(tiles - tail);
+      pl.tail_start = (int)(tiles - tiles % grid);
     }
   }
   pl.kb_per_split = (kb_total + pl.splits - 1) / pl.splits;
