@@ -11,6 +11,8 @@ Functions carry the C names:
   bf16 x (the bf16 entry point is ``dg_quantize_per_token_group_bf16``)
 * ``dg_quantize_per_block(w)``        -> (q uint8 like w, sb float32 ([G,] ceil(N/128), ceil(K/128)))
 * ``dg_gemm_fp8_nt(a, sa, b, sb)``    -> d bf16 (M, N)
+* ``dg_gemm_fp8_nt_act_quant(x, b, sb)`` -> d bf16 (M, N) from unquantized fp32 or bf16 x, its
+  per-token-group quantization done inside the GEMM launch
 * ``dg_gemm_fp8_grouped_contiguous(a, sa, b, sb, m_indices)``  -> d bf16 (M_total, N)
 * ``dg_gemm_fp8_grouped_masked(a, sa, b, sb, masked_m)``       -> d bf16 (G, M_max, N)
 * training-side layouts: ``dg_quantize_per_channel_group(x)`` -> (qt uint8 (K, M), st float32
@@ -51,6 +53,11 @@ _SIGNATURES = {
     "dg_quantize_per_block": (ctypes.c_int, [_vp, _c_int64, _c_int64, _c_int64, _vp, _vp, _vp]),
     "dg_gemm_fp8_nt": (ctypes.c_int, [_vp, _vp, _c_int64, _vp, _vp, _vp, _c_int64, _c_int64, _c_int64,
                                       _vp, ctypes.c_size_t, _vp]),
+    "dg_gemm_fp8_nt_act_quant": (ctypes.c_int, [_vp, _vp, _vp, _vp, _c_int64, _c_int64, _c_int64, _vp,
+                                                ctypes.c_size_t, _vp]),
+    "dg_gemm_fp8_nt_act_quant_bf16": (ctypes.c_int, [_vp, _vp, _vp, _vp, _c_int64, _c_int64, _c_int64, _vp,
+                                                     ctypes.c_size_t, _vp]),
+    "dg_gemm_fp8_nt_act_quant_workspace_size": (ctypes.c_size_t, [_c_int64, _c_int64, _c_int64]),
     "dg_gemm_fp8_grouped_contiguous": (ctypes.c_int, [_vp, _vp, _c_int64, _vp, _vp, _vp, _c_int64, _vp,
                                                       _c_int64, _c_int64, _c_int64, _vp]),
     "dg_gemm_fp8_grouped_masked": (ctypes.c_int, [_vp, _vp, _c_int64, _vp, _vp, _vp, _vp, _c_int64,
@@ -286,6 +293,37 @@ def dg_gemm_fp8_nt(a, sa, b, sb, d=None, workspace=None, use_workspace=True):
            lib().dg_gemm_fp8_nt(_ptr(a), _ptr(sa), sa.shape[-1], _ptr(b), _ptr(sb), _ptr(d), m, n, k,
                                 _ptr(workspace), ws_bytes, _stream(a)))
     return d
+
+
+def dg_gemm_fp8_nt_act_quant_workspace_size(m, n, k):
+    return int(lib().dg_gemm_fp8_nt_act_quant_workspace_size(int(m), int(n), int(k)))
+
+
+def dg_gemm_fp8_nt_act_quant(x, b, sb, d=None, workspace=None):
+    """D (M, N) bf16 = A (M, K) * B (N, K)^T where (A, sa) is the per-token-group quantization of
+    x (float32 or bfloat16 (M, K)), done inside the GEMM launch.  The workspace is required (by
+    default a zero-filled one per device); the result is bit-identical to
+    dg_quantize_per_token_group(x) followed by dg_gemm_fp8_nt."""
+    _require(x.dtype in (torch.float32, torch.bfloat16) and x.dim() == 2, "x must be float32 or bfloat16 (M, K)")
+    b = _bytes(b)
+    m, k = x.shape
+    n = b.shape[0]
+    if d is None:
+        d = torch.empty((m, n), dtype=torch.bfloat16, device=x.device)
+    _dev(x, b, sb, d)
+    if workspace is None:
+        workspace = default_workspace(x.device, dg_gemm_fp8_nt_act_quant_workspace_size(m, n, k))
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    name = "dg_gemm_fp8_nt_act_quant" + ("_bf16" if x.dtype == torch.bfloat16 else "")
+    _check(name, getattr(lib(), name)(_ptr(x), _ptr(b), _ptr(sb), _ptr(d), m, n, k, _ptr(workspace), ws_bytes,
+                                      _stream(x)))
+    return d
+
+
+def dg_gemm_fp8_nt_act_quant_bf16(x, b, sb, d=None, workspace=None):
+    """bfloat16 x (M, K): dg_gemm_fp8_nt_act_quant_bf16."""
+    _require(x.dtype == torch.bfloat16, "x must be bfloat16")
+    return dg_gemm_fp8_nt_act_quant(x, b, sb, d=d, workspace=workspace)
 
 
 def dg_gemm_fp8_nt_row_scaled(a, sa, b, sb, d=None, workspace=None, use_workspace=True):

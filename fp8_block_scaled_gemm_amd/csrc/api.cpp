@@ -33,6 +33,9 @@ int launch_gemm(int layout, const uint8_t* a, const float* sa, int64_t ld_sa, co
                 int64_t groups, int64_t m, int64_t n, int64_t k, void* ws, size_t ws_bytes,
                 hipStream_t stream, int num_cus);
 size_t gemm_workspace_size(int64_t m, int64_t n, int64_t k, int64_t groups, int num_cus);
+int launch_gemm_fq(const void* x, bool x_bf16, const uint8_t* b, const float* sb, uint16_t* d, int64_t m, int64_t n,
+                   int64_t k, void* ws, size_t ws_bytes, hipStream_t stream, int num_cus);
+size_t gemm_fq_workspace_size(int64_t m, int64_t n, int64_t k, int num_cus);
 void gemm_config_name(int layout, int64_t m, int64_t n, int64_t k, int64_t groups, int num_cus, char* buf,
                       size_t len);
 
@@ -180,6 +183,38 @@ int dg_gemm_fp8_nt(const uint8_t* a, const float* sa, int64_t ld_sa, const uint8
   if (cus < 0) return cus;
   return launch_gemm(0, a, sa, ld_sa, b, sb, 0, 0, d, nullptr, nullptr, 1, m, n, k, workspace,
                      workspace ? workspace_bytes : 0, static_cast<hipStream_t>(stream), cus);
+}
+
+size_t dg_gemm_fp8_nt_act_quant_workspace_size(int64_t m, int64_t n, int64_t k) {
+  if (m <= 0 || n <= 0 || k <= 0 || k % kKAlign) return 0;
+  const int cus = effective_cus();
+  if (cus < 0) return 0;
+  return gemm_fq_workspace_size(m, n, k, cus);
+}
+
+static int gemm_act_quant(const void* x, bool bf16, const uint8_t* b, const float* sb, uint16_t* d, int64_t m,
+                          int64_t n, int64_t k, void* workspace, size_t workspace_bytes, dg_stream_t stream) {
+  DG_REQUIRE(m >= 0 && n >= 0 && k > 0 && k % kKAlign == 0,
+             "gemm_act_quant: need m >= 0, n >= 0, k > 0, k %% 16 == 0 (m=%lld n=%lld k=%lld)", (long long)m,
+             (long long)n, (long long)k);
+  DG_REQUIRE(m <= 0x7fffffffLL && n <= 0x7fffffffLL && k <= 0x7fffffffLL, "gemm_act_quant: dimension too large");
+  if (m == 0 || n == 0) return DG_OK;
+  DG_REQUIRE(x && b && sb && d && workspace, "gemm_act_quant: null pointer");
+  DG_REQUIRE(aligned16(x) && aligned16(b) && aligned16(sb) && aligned16(d) && aligned16(workspace),
+             "gemm_act_quant: pointers must be 16-byte aligned");
+  const int cus = effective_cus();
+  if (cus < 0) return cus;
+  return launch_gemm_fq(x, bf16, b, sb, d, m, n, k, workspace, workspace_bytes, static_cast<hipStream_t>(stream), cus);
+}
+
+int dg_gemm_fp8_nt_act_quant(const float* x, const uint8_t* b, const float* sb, uint16_t* d, int64_t m, int64_t n,
+                             int64_t k, void* workspace, size_t workspace_bytes, dg_stream_t stream) {
+  return gemm_act_quant(x, false, b, sb, d, m, n, k, workspace, workspace_bytes, stream);
+}
+
+int dg_gemm_fp8_nt_act_quant_bf16(const uint16_t* x, const uint8_t* b, const float* sb, uint16_t* d, int64_t m,
+                                  int64_t n, int64_t k, void* workspace, size_t workspace_bytes, dg_stream_t stream) {
+  return gemm_act_quant(x, true, b, sb, d, m, n, k, workspace, workspace_bytes, stream);
 }
 
 int dg_gemm_fp8_grouped_contiguous(const uint8_t* a, const float* sa, int64_t ld_sa,

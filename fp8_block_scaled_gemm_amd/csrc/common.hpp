@@ -80,4 +80,26 @@ __device__ __forceinline__ float wave_max(float v) {
   return fmaxf(fmaxf(r0, r1), fmaxf(r2, r3));
 }
 
+// Four consecutive activations as fp32: fp32 input as is, bf16 input widened exactly (a bf16
+// value is the upper half of the fp32 word).  Streaming (nontemporal) loads: each is read once.
+__device__ __forceinline__ v4f load4(const float* p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const v4f*>(p));
+}
+__device__ __forceinline__ v4f load4(const uint16_t* p) {
+  typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+  const u32x2 w = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(p));
+  return v4f{__uint_as_float(w.x << 16), __uint_as_float(w.x & 0xffff0000u), __uint_as_float(w.y << 16),
+             __uint_as_float(w.y & 0xffff0000u)};
+}
+
+// One 1 x 128 group held by a half-wave (4 consecutive values per lane; values past k are zero):
+// s = amax / 448 (1 when amax = 0, IEEE division) into `s` on every lane, and the lane's 4 E4M3
+// bytes of fl32(v / s), rounded to nearest even and saturated, as the return value.  Fine-grained
+// scaling as proposed with DeepSeek-V3 (机器之心 DeepGEMM report, opening section).
+__device__ __forceinline__ uint32_t quant_group4(v4f v, float& s) {
+  const float amax = half_wave_max(fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w))));
+  s = amax == 0.0f ? 1.0f : amax / kE4M3Max;
+  return pack4_e4m3(clamp448(v.x / s), clamp448(v.y / s), clamp448(v.z / s), clamp448(v.w / s));
+}
+
 }  // namespace dg

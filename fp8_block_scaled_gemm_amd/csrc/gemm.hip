@@ -139,7 +139,111 @@ struct TileCoord {
   int g, mb, nbt, split, m_valid;
 };
 
-template <class C, int LAYOUT>
+// ---- activation quantization inside the GEMM launch (dense layout) ---------------------------
+// The 1 x 128 groups of x, numbered in row-major order (r * KB + kb), are cut into chunks of
+// kFqGroupsPerLane groups per half-wave.  Workgroups take chunks from a counter until none is
+// left, quantize them into a / sa with the per-token-group rule (quant_group4) through stores
+// that write through the XCD's L2 (the agent-scope stores of the split-K partials), wait for
+// those stores, and count the chunk as finished.  Every workgroup then waits until all chunks
+// are finished, and every wave acquires at device scope (its CU's L1 and its XCD's L2 drop
+// non-coherent lines), so the GEMM's ordinary loads read the quantized operand.  Nothing waits
+// inside a chunk and only a running workgroup takes one, so the wait ends however many of the
+// grid's workgroups are resident.
+constexpr int kFqGroupsPerLane = 4;   // groups per half-wave per chunk (loads in flight per lane)
+constexpr int kFqMaxPolls = 1 << 20;
+
+template <int NT, class T>
+__device__ __forceinline__ void fq_chunk(const GemmParams& p, const T* x, int c, int groups,
+                                         __amdgpu_buffer_rsrc_t rs_q, __amdgpu_buffer_rsrc_t rs_s) {
+  constexpr int kHalfWaves = NT / 32;
+  constexpr int kChunkGroups = kHalfWaves * kFqGroupsPerLane;
+  const int hw = threadIdx.x >> 5, l32 = threadIdx.x & 31;
+  int e[kFqGroupsPerLane], sidx[kFqGroupsPerLane];
+  bool ok[kFqGroupsPerLane];
+  v4f v[kFqGroupsPerLane];
+  // every lane loads (an absent group or column from x's first element), so the loads of all
+  // kFqGroupsPerLane groups are in flight together; absent values are zeroed afterwards
+#pragma unroll
+  for (int u = 0; u < kFqGroupsPerLane; ++u) {
+    const int gid = c * kChunkGroups + u * kHalfWaves + hw;
+    const bool present = gid < groups;
+    const int r = present ? gid / p.kb_total : 0;
+    const int kb = present ? gid - r * p.kb_total : 0;
+    const int col = kb * kGroup + 4 * l32;
+    ok[u] = present && col < p.k;
+    e[u] = r * p.k + col;
+    sidx[u] = present ? kb * (int)p.ld_sa + r : -1;
+    v[u] = load4(x + (ok[u] ? e[u] : 0));
+  }
+#pragma unroll
+  for (int u = 0; u < kFqGroupsPerLane; ++u)
+    if (!ok[u]) v[u] = v4f{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int u = 0; u < kFqGroupsPerLane; ++u) {
+    float s;
+    const uint32_t packed = quant_group4(v[u], s);
+    if (ok[u]) __builtin_amdgcn_raw_buffer_store_b32(packed, rs_q, e[u], 0, kCpolSc1);
+    if (l32 == 0 && sidx[u] >= 0) __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(s), rs_s, sidx[u] * 4, 0, kCpolSc1);
+  }
+}
+
+template <int NT>
+__device__ __forceinline__ void fused_act_quant(const GemmParams& p, int* s_bcast) {
+  constexpr int kChunkGroups = (NT / 32) * kFqGroupsPerLane;
+  const int tid = threadIdx.x;
+  const int groups = p.m * p.kb_total;   // m * k < 2^31 (host check)
+  const int chunks = (groups + kChunkGroups - 1) / kChunkGroups;
+  unsigned* const take = p.fq_sync;
+  unsigned* const done = p.fq_sync + 1;
+  const __amdgpu_buffer_rsrc_t rs_q = make_rsrc(p.a, (int64_t)p.m * p.k);
+  const __amdgpu_buffer_rsrc_t rs_s = make_rsrc(p.sa, (int64_t)p.kb_total * p.ld_sa * 4);
+  // One thread-0 region per iteration, between two barriers: it counts the previous chunk as
+  // finished (every thread waited for its stores of it, then reached the first barrier) and
+  // takes the next.  (Two thread-0 regions next to each other across the loop's back edge are
+  // merged by the compiler into one with a divergent latch, and the loop then never ends.)  The
+  // taken index is read as a wave-uniform scalar, so the loop's exit is a scalar branch.
+  bool had_chunk = false;
+  for (;;) {
+    __syncthreads();   // the previous chunk's stores are complete; the previous broadcast was read
+    if (tid == 0) {
+      if (had_chunk) __hip_atomic_fetch_add(done, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      *s_bcast = (int)__hip_atomic_fetch_add(take, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    __syncthreads();
+    const int c = __builtin_amdgcn_readfirstlane(*s_bcast);
+    if (c >= chunks) break;
+    if (p.fq_bf16) fq_chunk<NT>(p, static_cast<const uint16_t*>(p.fq_x), c, groups, rs_q, rs_s);
+    else fq_chunk<NT>(p, static_cast<const float*>(p.fq_x), c, groups, rs_q, rs_s);
+    __builtin_amdgcn_s_waitcnt(0);   // this thread's stores of the chunk have completed
+    had_chunk = true;
+  }
+  // Once every chunk is taken, the wait lasts about one chunk's time.  It gives up after
+  // kFqMaxPolls polls (on the order of a second) so that counters left non-zero by a misuse of
+  // the workspace give a wrong result instead of a wait that never ends.
+  if (tid == 0)
+    for (int poll = 0; poll < kFqMaxPolls; ++poll) {
+      if (__hip_atomic_load(done, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >= (unsigned)chunks) break;
+      __builtin_amdgcn_s_sleep(4);
+    }
+  __syncthreads();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+}
+
+// Leaving the kernel: the last workgroup out zeroes the counters of the quantization step for the
+// next call (every workgroup is past its wait by then).  Done here, after the persistent loop,
+// rather than right after the wait: a store there costs the main loop ~40 VGPRs.
+__device__ __forceinline__ void fused_act_quant_exit(const GemmParams& p) {
+  if (threadIdx.x != 0) return;
+  const unsigned prev = __hip_atomic_fetch_add(p.fq_sync + 2, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if (prev == gridDim.x - 1) {
+    __hip_atomic_store(p.fq_sync, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(p.fq_sync + 1, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(p.fq_sync + 2, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+}
+
+
+template <class C, int LAYOUT, bool FQ = false>
 __global__ __launch_bounds__(C::kThreads) void gemm_fp8_kernel(GemmParams p) {
   constexpr int NT = C::kThreads;
   constexpr int S = C::STAGES;
@@ -153,6 +257,7 @@ __global__ __launch_bounds__(C::kThreads) void gemm_fp8_kernel(GemmParams p) {
   __shared__ int s_scan[LAYOUT == kMasked ? 256 : 1];
   __shared__ int s_flag;
   static_assert(NT >= 256, "the masked-layout prefix needs 256 threads");
+  static_assert(!FQ || LAYOUT == kDense, "activation quantization in the launch: dense layout only");
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -163,6 +268,8 @@ __global__ __launch_bounds__(C::kThreads) void gemm_fp8_kernel(GemmParams p) {
   const int g4 = lane >> 4;
   const int wn0 = wave_n * C::WN;
   const int wm0 = wave_m * C::WM;
+
+  if constexpr (FQ) fused_act_quant<NT>(p, &s_flag);
 
   // ---- total work items -------------------------------------------------------
   int total_items;
@@ -535,6 +642,7 @@ __global__ __launch_bounds__(C::kThreads) void gemm_fp8_kernel(GemmParams p) {
       }
     }
   }
+  if constexpr (FQ) fused_act_quant_exit(p);
 }
 
 // ---------------------------------------------------------------------------
@@ -545,9 +653,9 @@ struct LaunchInfo {
   const void* fn;
 };
 
-template <class C, int LAYOUT>
+template <class C, int LAYOUT, bool FQ = false>
 static LaunchInfo info() {
-  void (*fn)(GemmParams) = gemm_fp8_kernel<C, LAYOUT>;
+  void (*fn)(GemmParams) = gemm_fp8_kernel<C, LAYOUT, FQ>;
   return LaunchInfo{C::BN, C::BM, C::kThreads, C::STAGES, reinterpret_cast<const void*>(fn)};
 }
 
@@ -569,18 +677,20 @@ using CfgWide = Cfg<256, 192, 128, 48, 2, true>;
 using CfgDec64 = Cfg<64, 64, 32, 32, 4>;
 using CfgDec128 = Cfg<64, 128, 32, 64, 3>;
 
-template <int LAYOUT>
+template <int LAYOUT, bool FQ = false>
 static LaunchInfo cfg_info(int cfg) {
   switch (cfg) {
     // per-row B scales hold one float4 per weight fragment row: the 256x192 tile's registers
     // have no room for them, so kDenseRowB runs its large shapes on 256x128
     case kCfgWide:
       if constexpr (LAYOUT == kDenseRowB) return info<CfgLarge, LAYOUT>();
-      else return info<CfgWide, LAYOUT>();
-    case kCfgDec64: return info<CfgDec64, LAYOUT>();
-    case kCfgDec128: return info<CfgDec128, LAYOUT>();
-    case kCfgRows128: return info<CfgRows128, LAYOUT>();
-    default: return info<CfgLarge, LAYOUT>();
+      else return info<CfgWide, LAYOUT, FQ>();
+    case kCfgDec64: return info<CfgDec64, LAYOUT, FQ>();
+    case kCfgDec128: return info<CfgDec128, LAYOUT, FQ>();
+    case kCfgRows128:
+      if constexpr (FQ) return info<CfgLarge, LAYOUT, FQ>();   // the dense plan never picks it
+      else return info<CfgRows128, LAYOUT>();
+    default: return info<CfgLarge, LAYOUT, FQ>();
   }
 }
 
@@ -762,9 +872,9 @@ size_t gemm_workspace_size(int64_t m, int64_t n, int64_t k, int64_t groups, int 
   return dense > rowb ? dense : rowb;
 }
 
-template <int LAYOUT>
+template <int LAYOUT, bool FQ = false>
 static int launch_layout(GemmParams p, const Plan& pl, hipStream_t stream, int num_cus) {
-  const LaunchInfo li = cfg_info<LAYOUT>(pl.cfg);
+  const LaunchInfo li = cfg_info<LAYOUT, FQ>(pl.cfg);
   const int occ = occupancy(li);
   const int64_t tiles = (int64_t)pl.tiles_m * pl.tiles_n * (LAYOUT == kContiguous ? 1 : p.num_groups);
   const int64_t items = pl.tail_start + (tiles - pl.tail_start) * pl.splits;
@@ -777,20 +887,10 @@ static int launch_layout(GemmParams p, const Plan& pl, hipStream_t stream, int n
   return e == hipSuccess ? kOk : set_error(kHip, "gemm launch: %s", hipGetErrorString(e));
 }
 
-int launch_gemm(int layout, const uint8_t* a, const float* sa, int64_t ld_sa, const uint8_t* b,
-                const float* sb, int64_t ld_sb, int64_t ld_ab, uint16_t* d, const int32_t* m_indices,
-                const int32_t* masked_m, int64_t groups, int64_t m, int64_t n, int64_t k, void* ws, size_t ws_bytes,
-                hipStream_t stream, int num_cus) {
-  const int64_t ld = ld_ab > 0 ? ld_ab : k;   // operand row stride (bytes)
-  if (n * ld > 0x7fffffffLL || m * ld > 0x7fffffffLL)
-    return set_error(kUnsupported, "gemm: one group's operand must be < 2^31 bytes (m=%lld n=%lld k=%lld ld=%lld)",
-                     (long long)m, (long long)n, (long long)k, (long long)ld);
-  if (layout == kMasked && groups > 1024) return set_error(kUnsupported, "masked gemm: at most 1024 groups");
-  const int64_t tile_groups = layout == kMasked ? groups : 1;
-  const bool can_split = (layout != kContiguous) && ws != nullptr;
-  Plan pl = make_plan(layout, m, n, k, tile_groups, num_cus, can_split);
-  if (pl.splits > 1 && ws_bytes < pl.ws_bytes) pl = make_plan(layout, m, n, k, tile_groups, num_cus, false);
-
+static GemmParams make_params(int layout, const Plan& pl, const uint8_t* a, const float* sa, int64_t ld_sa,
+                              const uint8_t* b, const float* sb, int64_t ld_sb, int64_t ld, uint16_t* d,
+                              const int32_t* m_indices, const int32_t* masked_m, int64_t groups, int64_t m, int64_t n,
+                              int64_t k) {
   GemmParams p{};
   p.a = a; p.sa = sa; p.b = b; p.sb = sb; p.d = d;
   p.m_indices = m_indices; p.masked_m = masked_m;
@@ -809,6 +909,24 @@ int launch_gemm(int layout, const uint8_t* a, const float* sa, int64_t ld_sa, co
   p.b_gstride = n * k;
   p.sb_gstride = (int64_t)p.nb128 * p.kb_total;
   p.d_gstride = m * n;
+  return p;
+}
+
+int launch_gemm(int layout, const uint8_t* a, const float* sa, int64_t ld_sa, const uint8_t* b,
+                const float* sb, int64_t ld_sb, int64_t ld_ab, uint16_t* d, const int32_t* m_indices,
+                const int32_t* masked_m, int64_t groups, int64_t m, int64_t n, int64_t k, void* ws, size_t ws_bytes,
+                hipStream_t stream, int num_cus) {
+  const int64_t ld = ld_ab > 0 ? ld_ab : k;   // operand row stride (bytes)
+  if (n * ld > 0x7fffffffLL || m * ld > 0x7fffffffLL)
+    return set_error(kUnsupported, "gemm: one group's operand must be < 2^31 bytes (m=%lld n=%lld k=%lld ld=%lld)",
+                     (long long)m, (long long)n, (long long)k, (long long)ld);
+  if (layout == kMasked && groups > 1024) return set_error(kUnsupported, "masked gemm: at most 1024 groups");
+  const int64_t tile_groups = layout == kMasked ? groups : 1;
+  const bool can_split = (layout != kContiguous) && ws != nullptr;
+  Plan pl = make_plan(layout, m, n, k, tile_groups, num_cus, can_split);
+  if (pl.splits > 1 && ws_bytes < pl.ws_bytes) pl = make_plan(layout, m, n, k, tile_groups, num_cus, false);
+
+  GemmParams p = make_params(layout, pl, a, sa, ld_sa, b, sb, ld_sb, ld, d, m_indices, masked_m, groups, m, n, k);
   if (pl.splits > 1) {
     p.counters = static_cast<unsigned*>(ws);
     p.ws = reinterpret_cast<float*>(static_cast<uint8_t*>(ws) + kCounterBytes);
@@ -819,6 +937,52 @@ int launch_gemm(int layout, const uint8_t* a, const float* sa, int64_t ld_sa, co
     case kDenseRowB: return launch_layout<kDenseRowB>(p, pl, stream, num_cus);
     default: return launch_layout<kDense>(p, pl, stream, num_cus);
   }
+}
+
+// ---- normal GEMM with the activation quantization inside the launch --------------------------
+// Workspace: the counter prefix (split-K arrival counters, the quantization step's counters in
+// its last words), then the E4M3 activations (m x k), their scales (KB x ld_sa, ld_sa = m
+// rounded up to 4), then the split-K partials of the same plan as the normal GEMM's.
+static size_t align256(size_t v) { return (v + 255) / 256 * 256; }
+
+struct FqLayout {
+  Plan pl;
+  int64_t ld_sa;
+  size_t q_off, s_off, partial_off, bytes;
+};
+
+static FqLayout fq_layout(int64_t m, int64_t n, int64_t k, int num_cus) {
+  FqLayout f;
+  f.pl = make_plan(kDense, m, n, k, 1, num_cus, true);
+  f.ld_sa = (m + 3) / 4 * 4;
+  const int64_t kb_total = (k + kGroup - 1) / kGroup;
+  f.q_off = kCounterBytes;
+  f.s_off = f.q_off + align256((size_t)(m * k));
+  f.partial_off = f.s_off + align256((size_t)(kb_total * f.ld_sa * 4));
+  f.bytes = f.partial_off + (f.pl.splits > 1 ? f.pl.ws_bytes - kCounterBytes : 0);
+  return f;
+}
+
+size_t gemm_fq_workspace_size(int64_t m, int64_t n, int64_t k, int num_cus) { return fq_layout(m, n, k, num_cus).bytes; }
+
+int launch_gemm_fq(const void* x, bool x_bf16, const uint8_t* b, const float* sb, uint16_t* d, int64_t m, int64_t n,
+                   int64_t k, void* ws, size_t ws_bytes, hipStream_t stream, int num_cus) {
+  if (n * k > 0x7fffffffLL || m * k > 0x7fffffffLL)
+    return set_error(kUnsupported, "gemm: one operand must be < 2^31 bytes (m=%lld n=%lld k=%lld)", (long long)m,
+                     (long long)n, (long long)k);
+  const FqLayout f = fq_layout(m, n, k, num_cus);
+  if (ws == nullptr || ws_bytes < f.bytes)
+    return set_error(kWorkspace, "gemm with activation quantization: workspace of %zu bytes, %zu needed", ws_bytes,
+                     f.bytes);
+  uint8_t* w = static_cast<uint8_t*>(ws);
+  GemmParams p = make_params(kDense, f.pl, w + f.q_off, reinterpret_cast<const float*>(w + f.s_off), f.ld_sa, b, sb, 0,
+                             k, d, nullptr, nullptr, 1, m, n, k);
+  p.counters = static_cast<unsigned*>(ws);
+  if (f.pl.splits > 1) p.ws = reinterpret_cast<float*>(w + f.partial_off);
+  p.fq_x = x;
+  p.fq_sync = static_cast<unsigned*>(ws) + kFqSyncWord;
+  p.fq_bf16 = x_bf16 ? 1 : 0;
+  return launch_layout<kDense, true>(p, f.pl, stream, num_cus);
 }
 
 // bf16 zero fill of count elements (count % 8 == 0, 16-byte aligned): the weight gradient of an

@@ -37,6 +37,12 @@ struct GemmParams {
   int kb_per_split;
   int tail_start;   // work items [0, tail_start) are whole tiles; every later tile is split in `splits`
   int nb128;        // ceil(n / 128): weight-scale rows per group
+  // Activation quantization inside the launch (dense layout): the unquantized activations
+  // (m x k row-major, fp32 or bf16) that the workgroups quantize into a / sa before the GEMM,
+  // and the three counters of that step (chunks taken, chunks finished, workgroups past the wait).
+  const void* fq_x;
+  unsigned* fq_sync;
+  int fq_bf16;
 };
 
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
@@ -106,7 +112,10 @@ constexpr int kMaxSplits = 16;   // K splits of one output tile at most
 // Split-K workspace: a fixed 64 KiB prefix of per-tile arrival counters (so that the partials of
 // one call never land where another call's counters are), then the fp32 partials.  Shapes with
 // more output tiles than counters do not split (they have plenty of tiles anyway).
+// The last 16 words of the prefix are not tile counters: the in-launch activation quantization
+// keeps its three counters there.
 constexpr size_t kCounterBytes = 64 * 1024;
-constexpr int64_t kMaxCounterTiles = kCounterBytes / 4;
+constexpr int64_t kFqSyncWord = kCounterBytes / 4 - 16;
+constexpr int64_t kMaxCounterTiles = kFqSyncWord;
 
 }  // namespace dg

@@ -26,18 +26,6 @@ constexpr int kTokThreads = 256;
 constexpr int kTokRows = kTokThreads / 32;   // rows per workgroup
 constexpr int kTokKb = 4;                    // K groups per workgroup (loads in flight per lane)
 
-// Four consecutive activations of a lane as fp32: fp32 input as is, bf16 input widened exactly
-// (a bf16 value is the upper half of the fp32 word).
-__device__ __forceinline__ v4f load4(const float* p) {
-  return __builtin_nontemporal_load(reinterpret_cast<const v4f*>(p));
-}
-__device__ __forceinline__ v4f load4(const uint16_t* p) {
-  typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
-  const u32x2 w = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(p));
-  return v4f{__uint_as_float(w.x << 16), __uint_as_float(w.x & 0xffff0000u), __uint_as_float(w.y << 16),
-             __uint_as_float(w.y & 0xffff0000u)};
-}
-
 template <class T>
 __global__ __launch_bounds__(kTokThreads) void quant_token_group_kernel(
     const T* __restrict__ x, int m, int k, uint8_t* __restrict__ q,
@@ -68,11 +56,8 @@ __global__ __launch_bounds__(kTokThreads) void quant_token_group_kernel(
 #pragma unroll
   for (int u = 0; u < kTokKb; ++u) {
     if (kb0 + u >= kbc) break;   // uniform
-    const float amax =
-        half_wave_max(fmaxf(fmaxf(fabsf(v[u].x), fabsf(v[u].y)), fmaxf(fabsf(v[u].z), fabsf(v[u].w))));
-    const float s = amax == 0.0f ? 1.0f : amax / kE4M3Max;
-    const uint32_t packed = pack4_e4m3(clamp448(v[u].x / s), clamp448(v[u].y / s),
-                                       clamp448(v[u].z / s), clamp448(v[u].w / s));
+    float s;
+    const uint32_t packed = quant_group4(v[u], s);
     if ((kb0 + u) * kGroup + 4 * lane < k) reinterpret_cast<uint32_t*>(dst + u * kGroup)[lane] = packed;
     if (lane == 0) scl[(int64_t)u * ld_sa] = s;
   }

@@ -62,7 +62,8 @@ enum dg_status {
   DG_OK = 0,
   DG_ERR_INVALID_ARG = -1, /* a pointer, size, stride or alignment is invalid */
   DG_ERR_UNSUPPORTED = -2, /* valid but outside what the kernels implement */
-  DG_ERR_WORKSPACE = -3,   /* reserved: workspace too small is not an error (split-K is skipped) */
+  DG_ERR_WORKSPACE = -3,   /* workspace too small where one is required (the GEMMs that take an
+                              optional workspace skip split-K instead) */
   DG_ERR_HIP = -4          /* a HIP runtime call failed */
 };
 
@@ -139,6 +140,34 @@ int dg_quantize_per_block(const float* w, int64_t num_groups, int64_t n, int64_t
 int dg_gemm_fp8_nt(const uint8_t* a, const float* sa, int64_t ld_sa, const uint8_t* b,
                    const float* sb, uint16_t* d, int64_t m, int64_t n, int64_t k, void* workspace,
                    size_t workspace_bytes, dg_stream_t stream);
+
+/*
+ * Normal FP8 GEMM on unquantized activations: D = A * B^T where A, sa are the per-token-group
+ * quantization of x (the rule of dg_quantize_per_token_group: 机器之心 report, opening section;
+ * ai.abqq.net summary, section 3), computed inside the GEMM launch instead of by a launch of
+ * its own.  The pages leave where the quantization runs open; the result is defined by the
+ * two steps it replaces.
+ * x  : fp32 (dg_gemm_fp8_nt_act_quant) or bf16 bits (..._bf16), (m, k) row-major, read only.
+ * b, sb, d, m, n, k : as dg_gemm_fp8_nt.
+ * workspace : required, at least dg_gemm_fp8_nt_act_quant_workspace_size(m, n, k) bytes.  It
+ *   holds the counters (its first 64 KiB: zero before the first use, e.g. a zero-filled
+ *   allocation, and left zero by every call), the quantized activations and their scales, and
+ *   the split-K partials.  Calls sharing one workspace must be ordered on one stream
+ *   (concurrent calls race); x and d must not overlap it.
+ * Result: bit-identical to dg_quantize_per_token_group(_bf16) of x (ld_sa = dg_get_scale_ld(m))
+ *   followed by dg_gemm_fp8_nt with a workspace of at least dg_gemm_workspace_size(m, n, k, 1)
+ *   bytes (the same tile plan and K split).
+ * Errors: DG_ERR_INVALID_ARG for null/misaligned pointers (16 bytes), negative sizes,
+ * k % 16 != 0; DG_ERR_WORKSPACE when the workspace is smaller than required;
+ * DG_ERR_UNSUPPORTED when m * k or n * k reaches 2^31.  Deterministic.
+ */
+int dg_gemm_fp8_nt_act_quant(const float* x, const uint8_t* b, const float* sb, uint16_t* d, int64_t m, int64_t n,
+                             int64_t k, void* workspace, size_t workspace_bytes, dg_stream_t stream);
+int dg_gemm_fp8_nt_act_quant_bf16(const uint16_t* x, const uint8_t* b, const float* sb, uint16_t* d, int64_t m,
+                                  int64_t n, int64_t k, void* workspace, size_t workspace_bytes, dg_stream_t stream);
+
+/* Workspace bytes dg_gemm_fp8_nt_act_quant(_bf16) needs for a shape (0 for invalid sizes). */
+size_t dg_gemm_fp8_nt_act_quant_workspace_size(int64_t m, int64_t n, int64_t k);
 
 /*
  * Contiguous-grouped MoE GEMM (3loumao explainer, section 03: every expert's

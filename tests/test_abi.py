@@ -89,6 +89,21 @@ def test_argument_validation(lib):
     assert lib.dg_gemm_fp8_nt(*args(4, 8, 128, 4, d=mis)) == DG_ERR_INVALID_ARG
     assert lib.dg_gemm_fp8_nt(*args(0, 8, 128, 0, a=None, d=None)) == DG_OK       # empty: no-op
     assert b"gemm" in lib.dg_last_error_message() or True
+    # dense GEMM with the activation quantization in the launch: the workspace is required
+    for fn in (lib.dg_gemm_fp8_nt_act_quant, lib.dg_gemm_fp8_nt_act_quant_bf16):
+        fargs = lambda m, n, k, x=fake, ws=fake, d=fake: (x, fake, fake, d, m, n, k, ws, 1 << 20, None)
+        assert fn(*fargs(4, 8, 100)) == DG_ERR_INVALID_ARG          # k % 16 != 0
+        assert fn(*fargs(4, 8, 0)) == DG_ERR_INVALID_ARG
+        assert fn(*fargs(-1, 8, 128)) == DG_ERR_INVALID_ARG
+        assert fn(*fargs(4, 8, 128, x=None)) == DG_ERR_INVALID_ARG
+        assert fn(*fargs(4, 8, 128, ws=None)) == DG_ERR_INVALID_ARG
+        assert b"null pointer" in lib.dg_last_error_message()
+        assert fn(*fargs(4, 8, 128, x=mis)) == DG_ERR_INVALID_ARG
+        assert fn(*fargs(4, 8, 128, ws=mis)) == DG_ERR_INVALID_ARG
+        assert fn(*fargs(0, 8, 128, x=None, ws=None, d=None)) == DG_OK   # empty: no-op
+        assert fn(*fargs(4, 0, 128, x=None, ws=None, d=None)) == DG_OK
+    assert lib.dg_gemm_fp8_nt_act_quant_workspace_size(4, 8, 100) == 0
+    assert lib.dg_gemm_fp8_nt_act_quant_workspace_size(0, 8, 128) == 0
     # contiguous: m_total must be 128-aligned, m_indices required
     assert lib.dg_gemm_fp8_grouped_contiguous(fake, fake, 100, fake, fake, fake, 2, fake, 100, 8, 128,
                                               None) == DG_ERR_INVALID_ARG
