@@ -64,6 +64,9 @@ def parse():
                     help="cap the GEMMs' persistent grid to this many CUs (dg_set_num_cus; 0 = all)")
     ap.add_argument("--act-dtype", default="fp32", choices=["fp32", "bf16"],
                     help="activation input type of the dense workloads (bf16: the bf16-input quantizer)")
+    ap.add_argument("--act-quant", default="separate", choices=["separate", "fused", "auto"],
+                    help="dense workloads: activation quantization as its own launch (separate), inside the "
+                         "GEMM launch (fused: dg_gemm_fp8_nt_act_quant), or inside it for M <= 128 only (auto)")
     ap.add_argument("--spin-ms", type=float, default=20.0,
                     help="device spin before each per-kernel timing pass (covers the host's enqueue time)")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -102,9 +105,23 @@ def quant_bytes(elems, k, in_bytes=4):
     return in_bytes * elems + elems + 4 * elems // 128
 
 
-def build_dense(torch, dg, dev, shapes, name, act_dtype="fp32"):
+def fused_gemm_bytes(m, n, k, in_bytes):
+    """Algorithmic HBM bytes of the GEMM that quantizes its activations in the launch: the
+    unquantized activations, B + its scales, bf16 D."""
+    return in_bytes * m * k + n * k + 4 * (-(-n // 128)) * (k // 128) + 2 * m * n
+
+
+def kernel_config(config):
+    """Kernel instance of a GEMM configuration name: the tile (the K split is a launch parameter
+    of the same kernel), and whether the activation quantization runs in the launch."""
+    return config.split("/split")[0] + (" +act-quant" if config.endswith("+act-quant") else "")
+
+
+def build_dense(torch, dg, dev, shapes, name, act_dtype="fp32", act_quant="separate"):
     """Ops for a list of dense (M, N, K) shapes sharing weights per (N, K).  act_dtype "bf16": the
-    activations arrive in bf16 and go through the bf16-input quantizer."""
+    activations arrive in bf16 and go through the bf16-input quantizer.  act_quant: "separate" =
+    a quantizer launch then the GEMM; "fused" = dg_gemm_fp8_nt_act_quant (quantization inside the
+    GEMM launch) for every shape; "auto" = fused for M <= 128, separate otherwise."""
     gen = Gen(torch, dev, 1234)
     ops = []
     weights = {}
@@ -117,18 +134,28 @@ def build_dense(torch, dg, dev, shapes, name, act_dtype="fp32"):
             ops.append(Op("wquant", f"wq {n}x{k}",
                           (lambda w32=w32, qb=qb, sb=sb: dg.dg_quantize_per_block(w32, q=qb, sb=sb)),
                           nbytes=quant_bytes(n * k, k)))
+    in_bytes = 2 if act_dtype == "bf16" else 4
     for (m, n, k) in shapes:
         w32, qb, sb = weights[(n, k)]
         a32 = gen.activations(m, k)
         if act_dtype == "bf16":
             a32 = a32.to(torch.bfloat16)
+        if act_quant == "fused" or (act_quant == "auto" and m <= 128):
+            d = torch.empty((m, n), dtype=torch.bfloat16, device=dev)
+            ws = dg.default_workspace(dev, dg.dg_gemm_fp8_nt_act_quant_workspace_size(m, n, k))
+            ops.append(Op("gemm", f"{m}x{n}x{k}",
+                          (lambda a32=a32, qb=qb, sb=sb, d=d, ws=ws: dg.dg_gemm_fp8_nt_act_quant(a32, qb, sb, d=d,
+                                                                                                  workspace=ws)),
+                          flops=2.0 * m * n * k, nbytes=fused_gemm_bytes(m, n, k, in_bytes),
+                          config=dg.dg_gemm_config_name(0, m, n, k, 1) + " +act-quant"))
+            continue
         qa = torch.empty((m, k), dtype=torch.uint8, device=dev)
         sa = torch.empty((k // 128, dg.dg_get_scale_ld(m)), dtype=torch.float32, device=dev)
         d = torch.empty((m, n), dtype=torch.bfloat16, device=dev)
         ws = dg.default_workspace(dev, dg.dg_gemm_workspace_size(m, n, k, 1))
         ops.append(Op("aquant", f"aq {m}x{k}",
                       (lambda a32=a32, qa=qa, sa=sa: dg.dg_quantize_per_token_group(a32, q=qa, sa=sa)),
-                      nbytes=quant_bytes(m * k, k, 2 if act_dtype == "bf16" else 4)))
+                      nbytes=quant_bytes(m * k, k, in_bytes)))
         ops.append(Op("gemm", f"{m}x{n}x{k}",
                       (lambda qa=qa, sa=sa, qb=qb, sb=sb, d=d, ws=ws: dg.dg_gemm_fp8_nt(qa, sa, qb, sb, d=d,
                                                                                          workspace=ws)),
@@ -337,10 +364,12 @@ def build_masked(torch, dg, dev, cases):
     return ops
 
 
-def build_workload(name, torch, dg, dev, act_dtype="fp32"):
+def build_workload(name, torch, dg, dev, act_dtype="fp32", act_quant="separate"):
     from fp8_block_scaled_gemm_amd import inputs
     if act_dtype != "fp32" and name not in ("dense_v3", "small", "large_dense"):
         raise SystemExit(f"bench.py: --act-dtype {act_dtype} applies to the dense workloads only")
+    if act_quant != "separate" and name not in ("dense_v3", "small", "large_dense"):
+        raise SystemExit(f"bench.py: --act-quant {act_quant} applies to the dense workloads only")
     if name == "dense_v3":
         # decode shapes first, then prefill, then the second decode size: the weights read by the two
         # decode passes are separated by > 1 GB of traffic, so neither pass is served by the 256 MB MALL
@@ -348,7 +377,7 @@ def build_workload(name, torch, dg, dev, act_dtype="fp32"):
         shapes = [(m, n, k) for m in order for (n, k) in inputs.DENSE_V3_NK]
         desc = ("DeepSeek-V3 dense GEMMs: M in {64,128,4096} x (N,K) in {(2112,7168),(24576,1536),"
                 "(32768,512),(7168,16384),(4096,7168),(7168,2048)}; A~N(0,1) with 1% rows x100, B~N(0,0.02^2)")
-        return build_dense(torch, dg, dev, shapes, name, act_dtype), desc
+        return build_dense(torch, dg, dev, shapes, name, act_dtype, act_quant), desc
     if name == "train_v3":
         return (build_train(torch, dg, dev, 4096, inputs.DENSE_V3_NK),
                 "linear-layer training step at 4096 tokens for each DeepSeek-V3 (N,K) in {(2112,7168),(24576,1536),"
@@ -360,9 +389,9 @@ def build_workload(name, torch, dg, dev, act_dtype="fp32"):
                 "MoE layer training step over the contiguous layout: G=8, ~8192 tokens/expert (+-25%) padded to 128, "
                 "(N,K) in {(4096,7168),(7168,2048)}: forward, dgrad (transposed expert blocks), wgrad (k-grouped)")
     if name == "small":
-        return build_dense(torch, dg, dev, [(128, 512, 512)], name, act_dtype), "M=128, N=512, K=512"
+        return build_dense(torch, dg, dev, [(128, 512, 512)], name, act_dtype, act_quant), "M=128, N=512, K=512"
     if name == "large_dense":
-        return (build_dense(torch, dg, dev, [(16384, 7168, 16384)], name, act_dtype),
+        return (build_dense(torch, dg, dev, [(16384, 7168, 16384)], name, act_dtype, act_quant),
                 "dense prefill M=16384, N=7168, K=16384")
     if name == "contiguous":
         cases = []
@@ -572,7 +601,7 @@ def main():
     if args.workload == "overlap":
         overlap_bench(args, torch, dg, dev)
         return
-    ops, desc = build_workload(args.workload, torch, dg, dev, args.act_dtype)
+    ops, desc = build_workload(args.workload, torch, dg, dev, args.act_dtype, args.act_quant)
     torch.cuda.synchronize()
     print(f"[bench] workload {args.workload}: {len(ops)} ops per step", file=sys.stderr, flush=True)
 
@@ -661,7 +690,7 @@ def main():
     by_cfg = {}
     for op in ops:
         if op.kind == "gemm":
-            by_cfg.setdefault(op.config.split("/split")[0], []).append(op)
+            by_cfg.setdefault(kernel_config(op.config), []).append(op)
     dom_cfg, dom_ops = max(by_cfg.items(), key=lambda kv: sum(sum(o.times) for o in kv[1]))
     tot_t = sum(sum(o.times) for o in dom_ops) * 1e-3
     launches = sum(len(o.times) for o in dom_ops)
@@ -704,6 +733,7 @@ def main():
            "scaling": "weak", "vs_baseline": None, "dtype": "fp8_e4m3", "data": "synthetic",
            "config": {"workload": args.workload, "description": desc, "gemms": len(shapes),
                       "activation_input": args.act_dtype,
+                      "activation_quantization": args.act_quant,
                       "step": ("per (N,K): weight quantization + transpose; forward (quantize X, GEMM), dgrad "
                                "(quantize dY, GEMM with W^T), wgrad (per-channel quantize dY and X, row-scaled GEMM)"
                                if args.workload == "train_v3" else

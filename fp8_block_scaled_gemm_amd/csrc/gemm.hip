@@ -38,6 +38,12 @@
 //  * Small-m shapes split K over workgroups; the last-arriving workgroup of a
 //    tile sums the fp32 partials in fixed split order (deterministic) and stores
 //    bf16.
+//  * The normal form can also take unquantized activations (the FQ flag): a prologue
+//    quantizes them once into the workspace, shared by all workgroups through a work
+//    queue, before the unchanged main loop.  It costs one device-scope atomic per
+//    workgroup and one L2 invalidation per wave, which on this 8-XCD part exceed what
+//    a separate quantizer launch costs in a HIP graph; the two-launch path stays the
+//    faster one.
 #include <cstdio>
 #include <type_traits>
 

@@ -26,7 +26,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 
 
 # tile configuration of a gemm_fp8_kernel instance: BN, BM, WN, WM, STAGES (then optional flags), layout
-_CFG = re.compile(r"gemm_fp8_kernel<dg::Cfg<(\d+), (\d+), (\d+), (\d+), (\d+)(?:, \w+)*>, (\d)>")
+_CFG = re.compile(r"gemm_fp8_kernel<dg::Cfg<(\d+), (\d+), (\d+), (\d+), (\d+)(?:, \w+)*>, (\d)(?:, (true|false))?>")
 
 
 def short_name(name):
@@ -34,9 +34,10 @@ def short_name(name):
     'gemm_fp8_kernel 256x128/8waves (layout 0)'; other kernels: first 70 characters."""
     m = _CFG.search(name)
     if m:
-        bn, bm, wn, wm, _, lay = (int(v) for v in m.groups())
+        bn, bm, wn, wm, _, lay = (int(v) for v in m.groups()[:6])
         waves = (bn // wn) * (bm // wm)
-        return f"gemm_fp8_kernel {bn}x{bm}/{waves}waves (layout {lay})"
+        aq = ", activation quantization in the launch" if m.group(7) == "true" else ""
+        return f"gemm_fp8_kernel {bn}x{bm}/{waves}waves (layout {lay}{aq})"
     m = re.search(r"dg::(\w+_kernel)", name)
     if m:
         return m.group(1)
@@ -47,9 +48,11 @@ def gemm_config(name):
     m = _CFG.search(name)
     if not m:
         return None
-    bn, bm, wn, wm, _, layout = (int(v) for v in m.groups())
-    # layout 3 (per-row B scales) is labelled like bench.py's configuration of the row-scaled GEMM
-    return f"gemm_fp8_kernel {'rowscaled ' if layout == 3 else ''}{bn}x{bm}/{(bn // wn) * (bm // wm)}waves"
+    bn, bm, wn, wm, _, layout = (int(v) for v in m.groups()[:6])
+    # layout 3 (per-row B scales) is labelled like bench.py's configuration of the row-scaled GEMM,
+    # and so is the kernel that quantizes its activations in the launch
+    return (f"gemm_fp8_kernel {'rowscaled ' if layout == 3 else ''}{bn}x{bm}/{(bn // wn) * (bm // wm)}waves"
+            f"{' +act-quant' if m.group(7) == 'true' else ''}")
 
 
 def cmd_trace(args):
@@ -109,6 +112,8 @@ def cmd_traffic(args):
     alg = defaultdict(list)
     for sh in bench["shapes"]:
         cfg = "gemm_fp8_kernel " + sh["config"].split("/split")[0]
+        if sh["config"].endswith("+act-quant"):
+            cfg += " +act-quant"
         alg[cfg].append(sh["gbps"] * sh["us"] * 1e3)   # bytes = GB/s * us * 1e3
     ff, fk, fv = copy_factor(args.copy_fetch, "FETCH_SIZE")
     wf, wk, wv = copy_factor(args.copy_write, "WRITE_SIZE")
