@@ -153,7 +153,12 @@ int dg_gemm_fp8_nt(const uint8_t* a, const float* sa, int64_t ld_sa, const uint8
  *   holds the counters (its first 64 KiB: zero before the first use, e.g. a zero-filled
  *   allocation, and left zero by every call), the quantized activations and their scales, and
  *   the split-K partials.  Calls sharing one workspace must be ordered on one stream
- *   (concurrent calls race); x and d must not overlap it.
+ *   (concurrent calls race); x and d must not overlap it.  The workgroups of one call wait
+ *   for each other once (after the quantization); that wait is bounded, so counters that
+ *   are not zero on entry (a misuse of the workspace) give a wrong result, not a hang.
+ * Performance: on MI355X this form is slower than the two launches it replaces (the wait
+ *   across all workgroups costs more than a kernel boundary); it serves callers that need
+ *   a single launch.
  * Result: bit-identical to dg_quantize_per_token_group(_bf16) of x (ld_sa = dg_get_scale_ld(m))
  *   followed by dg_gemm_fp8_nt with a workspace of at least dg_gemm_workspace_size(m, n, k, 1)
  *   bytes (the same tile plan and K split).
