@@ -70,10 +70,13 @@ static int device_cus() {
   return cus;
 }
 
+// The CU count the planner uses: the device's, capped by dg_set_num_cus.  With no device
+// visible, a set cap stands in for it, so that the planning queries (configuration names,
+// workspace sizes) also answer on a host without a GPU; launches still fail there.
 static int effective_cus() {
-  const int cus = device_cus();
-  if (cus < 0) return cus;
   const int cap = g_cu_cap.load(std::memory_order_relaxed);
+  const int cus = device_cus();
+  if (cus < 0) return cap > 0 ? cap : cus;
   return (cap > 0 && cap < cus) ? cap : cus;
 }
 

@@ -657,12 +657,16 @@ __global__ __launch_bounds__(C::kThreads) void gemm_fp8_kernel(GemmParams p) {
 struct LaunchInfo {
   int bn, bm, threads, stages;
   const void* fn;
+  int lds_bytes;   // the kernel's static LDS: its __shared__ arrays
 };
 
 template <class C, int LAYOUT, bool FQ = false>
 static LaunchInfo info() {
   void (*fn)(GemmParams) = gemm_fp8_kernel<C, LAYOUT, FQ>;
-  return LaunchInfo{C::BN, C::BM, C::kThreads, C::STAGES, reinterpret_cast<const void*>(fn)};
+  constexpr int kStage = stage_bytes<C, LAYOUT>();
+  constexpr int kLds = 2 * kStage + (C::STAGES > 2 ? kStage : 16) + (C::STAGES > 3 ? kStage : 16) +
+                       4 * (LAYOUT == kMasked ? 1025 + 256 + 1 : 3);
+  return LaunchInfo{C::BN, C::BM, C::kThreads, C::STAGES, reinterpret_cast<const void*>(fn), kLds};
 }
 
 // Tile configurations: BN x BM workgroup tile, WN x WM wave tile, LDS stages.
@@ -700,10 +704,16 @@ static LaunchInfo cfg_info(int cfg) {
   }
 }
 
+// Workgroups per CU.  Without a device to ask (planning queries on a host without a GPU), the
+// LDS bound: 160 KB per CU over the kernel's static LDS, which is what limits every tile
+// configuration here (two 64-row tiles or one 256-row tile per CU).
 static int occupancy(const LaunchInfo& li) {
   int blocks = 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, li.fn, li.threads, 0) != hipSuccess || blocks < 1)
-    blocks = 1;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, li.fn, li.threads, 0) != hipSuccess || blocks < 1) {
+    (void)hipGetLastError();
+    blocks = 160 * 1024 / li.lds_bytes;
+    blocks = blocks < 1 ? 1 : blocks;
+  }
   return blocks;
 }
 

@@ -299,7 +299,9 @@ int dg_gemm_fp8_k_grouped_row_scaled(const uint8_t* a, const float* sa, int64_t 
 int dg_get_num_cus(void);
 
 /* Set that cap (1 <= n); n larger than the device's CU count is clamped.  Process-wide.
- * Returns DG_OK or DG_ERR_INVALID_ARG. */
+ * With no device visible, the cap stands in for the device's CU count in the planning
+ * queries below (dg_gemm_workspace_size, dg_gemm_config_name, ...), so that plans can be
+ * inspected on a host without a GPU.  Returns DG_OK or DG_ERR_INVALID_ARG. */
 int dg_set_num_cus(int n);
 
 /* Row alignment required of each group in the contiguous layout: 128. */

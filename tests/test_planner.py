@@ -1,0 +1,113 @@
+"""The GEMM planner on the host: tile configuration, K split and workspace size per shape.
+
+With no GPU visible, a CU cap set with dg_set_num_cus stands in for the device's CU count and
+the occupancy comes from each configuration's LDS, so the plans below are those the library
+makes on a 256-CU MI355X (the GPU tests and bench.py report the same names there).  The queries
+run in a subprocess: the cap is process-wide.
+"""
+
+import json
+import os
+import re
+import subprocess
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+LIB = os.path.join(ROOT, "fp8_block_scaled_gemm_amd", "libdg.so")
+
+_QUERY = r"""
+import json, sys
+sys.path.insert(0, {root!r})
+import fp8_block_scaled_gemm_amd as dg
+L = dg.lib()
+assert L.dg_set_num_cus({cus}) == 0
+out = []
+for (layout, m, n, k, g) in json.loads(sys.argv[1]):
+    out.append([layout, m, n, k, g, L.dg_gemm_config_name(layout, m, n, k, g).decode(),
+                L.dg_gemm_workspace_size(m, n, k, g),
+                L.dg_gemm_fp8_nt_act_quant_workspace_size(m, n, k) if layout == 0 else 0])
+print(json.dumps(out))
+"""
+
+
+def plans(cases, cus=256):
+    if not os.path.exists(LIB):
+        pytest.fail("libdg.so is not built: run `python -m fp8_block_scaled_gemm_amd._build`")
+    r = subprocess.run([sys.executable, "-c", _QUERY.format(root=ROOT, cus=cus), json.dumps(cases)],
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode == 0, r.stderr[-2000:]
+    return {tuple(row[:5]): tuple(row[5:]) for row in json.loads(r.stdout.strip().splitlines()[-1])}
+
+
+NAME = re.compile(r"^(\d+)x(\d+)/(\d+)waves/split(\d+)(?:\+tail(\d+))?$")
+
+# DeepSeek-V3 dense shapes (M, N, K) and the plan of each on 256 CUs
+V3_PLANS = {
+    (64, 2112, 7168): "64x64/4waves/split8", (64, 24576, 1536): "64x64/4waves/split1",
+    (64, 32768, 512): "64x64/4waves/split1", (64, 7168, 16384): "64x64/4waves/split4",
+    (64, 4096, 7168): "64x64/4waves/split4", (64, 7168, 2048): "64x64/4waves/split4",
+    (128, 2112, 7168): "64x64/4waves/split4", (128, 24576, 1536): "64x128/4waves/split1",
+    (128, 32768, 512): "64x128/4waves/split1", (128, 7168, 16384): "64x128/4waves/split4",
+    (128, 4096, 7168): "64x128/4waves/split4", (128, 7168, 2048): "64x64/4waves/split1",
+    (4096, 2112, 7168): "256x192/8waves/split1", (4096, 24576, 1536): "256x192/8waves/split1",
+    (4096, 32768, 512): "256x192/8waves/split1", (4096, 7168, 16384): "256x192/8waves/split1+tail2",
+    (4096, 4096, 7168): "256x192/8waves/split1+tail2", (4096, 7168, 2048): "256x192/8waves/split1",
+}
+
+
+def test_v3_dense_plans_on_256_cus():
+    got = plans([[0, m, n, k, 1] for (m, n, k) in V3_PLANS])
+    for (m, n, k), want in V3_PLANS.items():
+        name, ws, ws_fq = got[(0, m, n, k, 1)]
+        assert name == want, ((m, n, k), name, want)
+        splits = NAME.match(name)
+        split_plan = int(splits.group(4)) > 1 or splits.group(5) is not None
+        if split_plan:
+            assert ws > 0, (m, n, k, ws)
+        # the in-launch quantization's workspace: counters, E4M3 activations, scales, partials
+        ld = -(-m // 4) * 4
+        assert ws_fq >= 64 * 1024 + m * k + (k // 128) * ld * 4 + (max(ws - 64 * 1024, 0) if split_plan else 0)
+
+
+def test_split_last_round_plans():
+    """Shapes with a partial last round of the persistent grid and a long K split only that round
+    (the GPU tests assert the same names at 256 CUs)."""
+    got = plans([[0, 4608, 4096, 6144, 1], [0, 4096, 7168, 6144, 1], [3, 2048, 5120, 6144, 1],
+                 [0, 4096, 7168, 1024, 1]])
+    assert got[(0, 4608, 4096, 6144, 1)][0] == "256x192/8waves/split1+tail2"
+    assert got[(0, 4096, 7168, 6144, 1)][0] == "256x192/8waves/split1+tail2"
+    assert got[(3, 2048, 5120, 6144, 1)][0] == "256x128/8waves/split1+tail2"
+    assert "+tail" not in got[(0, 4096, 7168, 1024, 1)][0]   # pieces would be < 24 K blocks
+
+
+def test_plan_invariants_over_shapes():
+    ms = [1, 17, 64, 65, 128, 129, 256, 1000, 4096, 8192]
+    nks = [(128, 128), (512, 7168), (2112, 7168), (7168, 2048), (4096, 512), (24576, 1536), (300, 16400)]
+    cases = [[layout, m, n, k, 1] for layout in (0, 3) for m in ms for (n, k) in nks]
+    cases += [[1, 128 * g * 4, n, k, g] for g in (1, 4, 8) for (n, k) in nks]
+    cases += [[2, m, n, k, g] for g in (1, 8, 32) for m in (32, 256) for (n, k) in nks]
+    for cus in (256, 80, 7):
+        got = plans(cases, cus)
+        for (layout, m, n, k, g), (name, ws, _) in got.items():
+            mt = NAME.match(name)
+            assert mt, (layout, m, n, k, g, name)
+            bn, bm, waves, splits = (int(mt.group(i)) for i in range(1, 5))
+            tail = mt.group(5)
+            assert (bn, bm, waves) in {(64, 64, 4), (64, 128, 4), (256, 128, 8), (256, 192, 8)}, name
+            assert 1 <= splits <= 16 and (tail is None or splits == 1)
+            if tail is not None:
+                assert 2 <= int(tail) <= 16
+            if layout == 1:   # the contiguous form never splits K (no workspace argument)
+                assert splits == 1 and tail is None, name
+            if layout == 3:   # per-row B scales leave no registers for the 256x192 tile
+                assert (bn, bm) != (256, 192), name
+            if layout == 0 and m <= 128:   # few rows: the 64-row weight tiles
+                assert bn == 64, (m, name)
+            if layout in (0, 3) and m > 128:
+                assert bn == 256, (m, name)
+            if layout in (0, 2) and (splits > 1 or tail is not None):
+                assert ws > 0, (layout, m, n, k, g, name)   # a split plan has its workspace size
+            kb = -(-k // 128)
+            assert splits <= kb and int(tail or 1) <= kb
