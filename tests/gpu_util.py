@@ -104,3 +104,21 @@ def oracle_quant_blocks(w, chunk=512):
     parts = list(_pool().map(oracle.quant.quantize_per_block,
                              [w[i:i + chunk] for i in range(0, w.shape[0], chunk)]))
     return np.concatenate([p[0] for p in parts]), np.concatenate([p[1] for p in parts])
+
+
+def cu_masked_stream(first, count):
+    """A HIP stream whose kernels may only run on CUs [first, first + count)
+    (hipExtStreamCreateWithCUMask, default priority), wrapped for torch."""
+    import ctypes
+    total = torch.cuda.get_device_properties(0).multi_processor_count
+    hip = ctypes.CDLL("libamdhip64.so")
+    words = (total + 31) // 32
+    mask = [0] * words
+    for cu in range(first, min(first + count, total)):
+        mask[cu // 32] |= 1 << (cu % 32)
+    arr = (ctypes.c_uint32 * words)(*mask)
+    handle = ctypes.c_void_p()
+    err = hip.hipExtStreamCreateWithCUMask(ctypes.byref(handle), ctypes.c_uint32(words), arr)
+    if err != 0:
+        pytest.fail(f"hipExtStreamCreateWithCUMask failed ({err})")
+    return torch.cuda.ExternalStream(handle.value, device=device())

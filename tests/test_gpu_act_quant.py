@@ -15,7 +15,8 @@ import torch
 import fp8_block_scaled_gemm_amd as dg
 from fp8_block_scaled_gemm_amd import inputs
 import oracle
-from gpu_util import bf16_bits, check_gemm, device, oracle_quant_blocks, oracle_quant_rows, say, to_dev
+from gpu_util import (bf16_bits, check_gemm, cu_masked_stream, device, oracle_quant_blocks, oracle_quant_rows,
+                      say, to_dev)
 
 pytestmark = pytest.mark.gpu
 
@@ -105,6 +106,26 @@ def test_work_queue_with_a_small_grid():
         dg.dg_set_num_cus(old)
     assert np.array_equal(bf16_bits(d), bf16_bits(ref2))
     check_gemm(d, oracle_ref(x, qb, sb), "act-quant 2 CUs")
+
+
+@pytest.mark.parametrize("m,n,k", [(64, 4096, 7168), (512, 2048, 7168)])
+def test_full_grid_on_a_cu_masked_stream(m, n, k):
+    """The grid is planned for every CU, but the stream may only use 16 of them: most workgroups
+    start only after others have finished.  Chunks are taken only by running workgroups, so the
+    wait still ends; the result is the two launches' and the counters are left zero."""
+    x, xd, qb, sb = operands("actq_cumask", m, n, k)
+    b, sbd = to_dev(qb), to_dev(sb)
+    ws = torch.zeros(dg.dg_gemm_fp8_nt_act_quant_workspace_size(m, n, k), dtype=torch.uint8, device=device())
+    say("act-quant gemm on 16 CUs", m, n, k, dg.dg_gemm_config_name(0, m, n, k))
+    torch.cuda.synchronize()
+    s = cu_masked_stream(0, 16)
+    with torch.cuda.stream(s):
+        d = dg.dg_gemm_fp8_nt_act_quant(xd, b, sbd, workspace=ws)
+    s.synchronize()
+    ref2 = two_step(xd, b, sbd)
+    torch.cuda.synchronize()
+    assert np.array_equal(bf16_bits(d), bf16_bits(ref2))
+    assert int(ws[:64 << 10].count_nonzero()) == 0
 
 
 def test_shared_workspace_sequence_leaves_counters_zero():
