@@ -435,7 +435,7 @@ def cpu_baseline(workload, seconds):
     rng = inputs.rng_for("cpu_sample")
 
     def run(rows_b):
-        flops, t = 0.0, 0.0
+        flops, t, per_shape = 0.0, 0.0, []
         for (n, k) in nk:
             a = inputs.activations_with_outliers(rng, 128 if train else 64, k)
             b = inputs.normal(rng, (min(rows_b, n), k), 0.02)
@@ -452,12 +452,25 @@ def cpu_baseline(workload, seconds):
                 qb, sb = oracle.quant.quantize_per_block(b)
                 oracle.gemm.gemm_nt(qa, sa, qb, sb)
                 flops += 2.0 * 64 * b.shape[0] * k
-            t += time.perf_counter() - t0
-        return flops, t
+            per_shape.append(time.perf_counter() - t0)
+            t += per_shape[-1]
+        return flops, t, per_shape
 
-    f0, t0 = run(128)                     # calibration
-    rows_b = int(max(128, min(8192, 128 * seconds / max(t0, 1e-3))) // 128 * 128)
-    f, t = run(rows_b)
+    # calibration: each shape's time at 128 and 384 weight rows, as a fixed part (the activation
+    # rows) plus a part per weight row
+    _, _, c1 = run(128)
+    _, _, c3 = run(384)
+    per_row = [max((b - a) / 256, 1e-9) for a, b in zip(c1, c3)]
+    fixed = [max(a - 128 * r, 0.0) for a, r in zip(c1, per_row)]
+    max_n = max(n for (n, _) in nk)
+
+    def predicted(rows):                  # the sample rows of a shape are capped at its N
+        return sum(f + r * min(rows, n) for f, r, (n, _) in zip(fixed, per_row, nk))
+
+    rows_b = 128
+    while rows_b < max_n and predicted(rows_b + 128) <= seconds:
+        rows_b += 128
+    f, t, _ = run(rows_b)
     return {"value": f / t / 1e12, "unit": "TFLOP/s", "cores": int(blas_threads), "kind": "oracle",
             "sample": ((f"oracle forward + dgrad + wgrad of 128 tokens x {rows_b} weight rows for each (N,K) "
                         if train else
