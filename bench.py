@@ -427,7 +427,7 @@ def cpu_baseline(workload, seconds):
         blas_threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
     except Exception:
         blas_threads = 1
-    # sample: for each (N, K) of the dense V3 set, 64 activation rows x `rows_b` weight rows through
+    # sample: for each (N, K) of the dense V3 set, 128 activation rows x `rows_b` weight rows through
     # the whole oracle path (quantize A rows, quantize B rows, fp64 GEMM); rows_b scaled to the budget
     nk = (inputs.DENSE_V3_NK if workload in ("dense_v3", "train_v3") else
           inputs.GROUPED_NK if workload == "train_moe" else [(512, 512)])
@@ -437,7 +437,7 @@ def cpu_baseline(workload, seconds):
     def run(rows_b):
         flops, t, per_shape = 0.0, 0.0, []
         for (n, k) in nk:
-            a = inputs.activations_with_outliers(rng, 128 if train else 64, k)
+            a = inputs.activations_with_outliers(rng, 128, k)
             b = inputs.normal(rng, (min(rows_b, n), k), 0.02)
             t0 = time.perf_counter()
             if train:   # forward, dgrad and wgrad of the sampled slice through the oracle
@@ -451,7 +451,7 @@ def cpu_baseline(workload, seconds):
                 qa, sa = oracle.quant.quantize_per_token_group(a)
                 qb, sb = oracle.quant.quantize_per_block(b)
                 oracle.gemm.gemm_nt(qa, sa, qb, sb)
-                flops += 2.0 * 64 * b.shape[0] * k
+                flops += 2.0 * a.shape[0] * b.shape[0] * k
             per_shape.append(time.perf_counter() - t0)
             t += per_shape[-1]
         return flops, t, per_shape
@@ -474,7 +474,7 @@ def cpu_baseline(workload, seconds):
     return {"value": f / t / 1e12, "unit": "TFLOP/s", "cores": int(blas_threads), "kind": "oracle",
             "sample": ((f"oracle forward + dgrad + wgrad of 128 tokens x {rows_b} weight rows for each (N,K) "
                         if train else
-                        f"oracle quantize + fp64 GEMM of 64 activation rows x {rows_b} weight rows for each (N,K) ")
+                        f"oracle quantize + fp64 GEMM of 128 activation rows x {rows_b} weight rows for each (N,K) ")
                        + f"of the workload ({f / 1e9:.2f} GFLOP in {t:.1f} s; quantization single-threaded numpy, "
                        f"GEMM on {blas_threads} BLAS threads)"),
             "seconds": t}
