@@ -1,6 +1,7 @@
 """Summaries of rocprofv3 runs of bench.py for profiles/ (measurement tooling, runs on the host).
 
     python profile_summary.py trace <kernel_trace.csv> --out profiles/<name>.md --command "<cmd>"
+    python profile_summary.py mfma <counter_collection.csv> --out profiles/<name>.md --command "<cmd>"
     python profile_summary.py traffic --workload dense_v3 --bench-json <bench.json>
         --fetch <counter_collection.csv> --write <counter_collection.csv>
         --copy-fetch <counter_collection.csv> --copy-write <counter_collection.csv>
@@ -154,6 +155,43 @@ def cmd_traffic(args):
     print("\n".join(lines))
 
 
+def cmd_mfma(args):
+    """MFMA-pipe utilisation per GEMM tile configuration from SQ_VALU_MFMA_BUSY_CYCLES (summed over
+    the 1024 SIMDs), SQ_INSTS_MFMA and GRBM_GUI_ACTIVE (summed over the 8 XCDs), per dispatch."""
+    import statistics
+    acc = defaultdict(lambda: defaultdict(float))
+    meta = {}
+    with open(args.csv) as fh:
+        for r in csv.DictReader(fh):
+            d = int(r["Dispatch_Id"])
+            acc[d][r["Counter_Name"]] += float(r["Counter_Value"])
+            meta[d] = (r["Kernel_Name"], int(r["End_Timestamp"]) - int(r["Start_Timestamp"]))
+    per = defaultdict(list)
+    for d, c in acc.items():
+        cfg = gemm_config(meta[d][0])
+        if not cfg or not c.get("GRBM_GUI_ACTIVE"):
+            continue
+        busy = c["SQ_VALU_MFMA_BUSY_CYCLES"] / args.simds            # MFMA-pipe cycles per SIMD
+        gui = c["GRBM_GUI_ACTIVE"] / args.xcds                      # active cycles of one XCD
+        per[cfg].append((busy / gui, busy / (meta[d][1] * args.clock_ghz),
+                         c["SQ_VALU_MFMA_BUSY_CYCLES"] / (32 * c["SQ_INSTS_MFMA"]), meta[d][1] / 1e3, gui / meta[d][1]))
+    lines = [f"# MFMA utilisation per GEMM tile configuration ({args.workload}): rocprofv3 counters", "",
+             "Command:", "", "```", args.command, "```", "",
+             f"Per dispatch: MFMA-pipe cycles per SIMD = SQ_VALU_MFMA_BUSY_CYCLES / {args.simds}; utilisation = "
+             f"that over the XCD's active cycles (GRBM_GUI_ACTIVE / {args.xcds}: the counter is summed over the "
+             f"XCDs), and over the dispatch's duration at {args.clock_ghz} GHz.  SQ_VALU_MFMA_BUSY_CYCLES equals "
+             "32 cycles per 16x16x128 FP8 MFMA (SQ_INSTS_MFMA), the instruction's pipe occupancy at the "
+             "published 5.0 PFLOP/s dense FP8 peak.", "",
+             "| kernel | dispatches | MFMA util (active cycles) | MFMA util (duration, %.1f GHz) | busy / (32 x MFMAs) | avg us | active cycles per ns |" % args.clock_ghz,
+             "|---|---|---|---|---|---|---|"]
+    for cfg, v in sorted(per.items()):
+        m = lambda i: statistics.mean(x[i] for x in v)
+        lines.append(f"| {cfg} | {len(v)} | {100 * m(0):.1f}% | {100 * m(1):.1f}% | {m(2):.3f} | {m(3):.1f} | {m(4):.2f} |")
+    with open(args.out, "w") as fh:
+        fh.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
 def main():
     ap = argparse.ArgumentParser()
     sub = ap.add_subparsers(dest="cmd", required=True)
@@ -166,8 +204,16 @@ def main():
     for a in ("--bench-json", "--fetch", "--write", "--copy-fetch", "--copy-write", "--out-md", "--out-json",
               "--command", "--workload"):
         c.add_argument(a, required=True)
+    mf = sub.add_parser("mfma")
+    mf.add_argument("csv")
+    mf.add_argument("--out", required=True)
+    mf.add_argument("--command", required=True)
+    mf.add_argument("--workload", default="dense_v3")
+    mf.add_argument("--simds", type=int, default=1024)
+    mf.add_argument("--xcds", type=int, default=8)
+    mf.add_argument("--clock-ghz", type=float, default=2.4)
     args = ap.parse_args()
-    {"trace": cmd_trace, "traffic": cmd_traffic}[args.cmd](args)
+    {"trace": cmd_trace, "traffic": cmd_traffic, "mfma": cmd_mfma}[args.cmd](args)
 
 
 if __name__ == "__main__":
