@@ -6,10 +6,9 @@ module that both the HIP path's tests/bench and the CPU oracle's checks feed
 from.  Only numpy is imported at module level; ``DeviceGen`` draws the same
 distributions with torch's seeded generator on a device, for inputs of many GB.
 
-Workloads (the pages measure "every shape DeepSeek-V3/R1 inference may use,
-prefill and decode, without tensor parallelism" - 机器之心 DeepGEMM report,
-"performance"; that shape set is not a public dataset, so these seeded,
-V3-shaped synthetic workloads stand in for it):
+Workloads (the pages benchmark the GEMM shapes of DeepSeek-V3/R1 inference, prefill and
+decode, with no tensor parallelism - 机器之心 DeepGEMM report, "performance"; that shape set is
+not a public dataset, so these seeded, V3-shaped synthetic workloads stand in for it):
 
 * ``small``        M=128, N=512, K=512; A, B ~ N(0, 1).
 * ``dense_v3``     M in {64, 128, 4096} x (N, K) in six V3 projection shapes;

@@ -293,6 +293,40 @@ def pin_quant_block_edges(seed=17):
     assert np.array_equal(q2[128:], q[128:]) and np.array_equal(q2[:128, :128], q[:128, :128])
 
 
+def pin_quant_block_grouped(seed=19):
+    """Grouped weights (G, N, K): every group's blocks take their scale from that group's own
+    elements only.  Three groups of magnitudes 1e-3, 1 and 1e3 (so a scale shared across groups, or
+    one group's blocks reused for another, is off by orders of magnitude), N = 200 (a partial
+    72-row block).  Each block scale is checked against the exact amax / 448 rounded to fp32,
+    sampled rows of every block against the scalar brute-force encoder, and a power-of-two change
+    of one group must move that group's scales only."""
+    rng = np.random.default_rng(seed)
+    g, n, k = 3, 200, 256
+    mags = [1e-3, 1.0, 1e3]
+    w = np.stack([(rng.standard_normal((n, k)) * mags[e]).astype(np.float32) for e in range(g)])
+    w[2, 190, 200] = np.float32(-4.5e3)   # the partial block of the last group holds its largest value
+    q, sb = oracle.quant.quantize_per_block_grouped(w)
+    assert q.shape == (g, n, k) and q.dtype == np.uint8
+    assert sb.shape == (g, 2, 2) and sb.dtype == np.float32
+    for e in range(g):
+        for i in range(2):
+            for kb in range(2):
+                blk = w[e, 128 * i:min(n, 128 * i + 128), 128 * kb:128 * kb + 128]
+                assert sb[e, i, kb] == rn32(Fraction(float(np.max(np.abs(blk)))) / 448), (e, i, kb)
+        for r in (0, 127, 128, 199):      # first and last row of each 128-row block
+            for kb in range(2):
+                s = sb[e, r // 128, kb]
+                cols = range(128 * kb, 128 * kb + 128, 5)
+                want = [brute_encode(rn32(Fraction(float(w[e, r, c])) / Fraction(float(s)))) for c in cols]
+                assert np.array_equal(q[e, r, list(cols)], np.array(want, np.uint8)), (e, r, kb)
+    w2 = w.copy()
+    w2[1] *= np.float32(2.0 ** 5)
+    q2, sb2 = oracle.quant.quantize_per_block_grouped(w2)
+    assert np.array_equal(q2, q)
+    assert np.array_equal(sb2[1], (sb[1] * np.float32(32.0)).astype(np.float32))
+    assert np.array_equal(sb2[0], sb[0]) and np.array_equal(sb2[2], sb[2])
+
+
 # --------------------------------------------------------------------------
 # GEMM pins
 # --------------------------------------------------------------------------
@@ -662,7 +696,7 @@ ALL_PINS = [
     pin_e4m3_named_codes, pin_e4m3_decode_vs_torch, pin_e4m3_roundtrip, pin_e4m3_encode_vs_torch,
     pin_e4m3_ties_and_saturation, pin_e4m3_brute_force_sample,
     pin_quant_brute_force, pin_quant_near_ties, pin_quant_one_hot, pin_quant_representable,
-    pin_quant_pow2_invariance, pin_quant_zero_group, pin_quant_block_edges,
+    pin_quant_pow2_invariance, pin_quant_zero_group, pin_quant_block_edges, pin_quant_block_grouped,
     pin_gemm_exact_rational, pin_gemm_all_448, pin_gemm_hadamard, pin_gemm_one_hot,
     pin_gemm_invariants, pin_gemm_grouped,
     pin_bf16_decode_vs_torch, pin_bf16_named_values, pin_quant_bf16_matches_widened,

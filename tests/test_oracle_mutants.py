@@ -90,6 +90,37 @@ def _quant_block_whole_panel(w):
     return q, sb
 
 
+_orig_block_grouped = Q.quantize_per_block_grouped
+
+
+def _block_grouped_reuses_group0(w):
+    """Every group quantized with group 0's blocks."""
+    w = np.asarray(w, dtype=np.float32)
+    q0, s0 = _orig_block(w[0])
+    return np.stack([q0] * w.shape[0]), np.stack([s0] * w.shape[0])
+
+
+def _block_grouped_shared_scale(w):
+    """One scale per (N block, K block) taken over all groups together."""
+    w = np.asarray(w, dtype=np.float32)
+    g, n, k = w.shape
+    amax = np.zeros((-(-n // 128), k // 128), np.float32)
+    for e in range(g):
+        for i in range(amax.shape[0]):
+            blk = w[e, 128 * i:128 * i + 128].reshape(-1, k // 128, 128)
+            amax[i] = np.maximum(amax[i], np.max(np.abs(blk), axis=(0, 2)))
+    s = np.where(amax == 0, np.float32(1), amax / np.float32(448)).astype(np.float32)
+    rows = np.repeat(s, 128, axis=0)[:n]                          # (n, k/128)
+    q = np.stack([E.encode((w[e].reshape(n, k // 128, 128) / rows[:, :, None]).astype(np.float32)).reshape(n, k)
+                  for e in range(g)])
+    return q, np.stack([s] * g)
+
+
+def _block_grouped_swaps_outputs(w):
+    q, s = _orig_block_grouped(w)
+    return s, q
+
+
 def _gemm_no_sb(qa, sa, qb, sb):
     return G.dequantize_rows(qa, sa) @ E.decode(qb).T
 
@@ -204,6 +235,9 @@ MUTANTS = {
     "quant_reciprocal_multiply": (Q, "quantize_per_token_group", _quant_tok_reciprocal),
     "quant_fp64_division": (Q, "quantize_per_token_group", _quant_tok_fp64_division),
     "quant_block_whole_panel": (Q, "quantize_per_block", _quant_block_whole_panel),
+    "block_grouped_reuses_group0": (Q, "quantize_per_block_grouped", _block_grouped_reuses_group0),
+    "block_grouped_shared_scale": (Q, "quantize_per_block_grouped", _block_grouped_shared_scale),
+    "block_grouped_swaps_outputs": (Q, "quantize_per_block_grouped", _block_grouped_swaps_outputs),
     "gemm_drops_weight_scale": (G, "gemm_nt", _gemm_no_sb),
     "gemm_weight_scale_index_mod": (G, "gemm_nt", _gemm_sb_mod),
     "gemm_act_scale_kb_reversed": (G, "gemm_nt", _gemm_sa_reversed_kb),
