@@ -77,7 +77,12 @@ _SIGNATURES = {
     "dg_get_scale_ld": (_c_int64, [_c_int64]),
     "dg_gemm_workspace_size": (ctypes.c_size_t, [_c_int64, _c_int64, _c_int64, _c_int64]),
     "dg_gemm_config_name": (ctypes.c_char_p, [ctypes.c_int, _c_int64, _c_int64, _c_int64, _c_int64]),
+    "dg_get_debug_status": (ctypes.c_int, [ctypes.POINTER(ctypes.c_uint32), ctypes.POINTER(_c_int64), ctypes.c_int]),
 }
+
+DG_DIAG_MIXED_BLOCK = 1
+DG_DIAG_EXPERT_RANGE = 2
+DG_DIAG_FQ_TIMEOUT = 4
 
 
 def lib():
@@ -167,17 +172,40 @@ def dg_gemm_config_name(layout, m, n, k, num_groups=1):
     return lib().dg_gemm_config_name(int(layout), int(m), int(n), int(k), int(num_groups)).decode()
 
 
+def dg_get_debug_status(clear=True):
+    """(flags, block): the sticky device diagnostics (DG_DIAG_* bits) of the current device and the
+    first 128-row block a contiguous-layout check found wrong (-1 if none).  Synchronises."""
+    flags, block = ctypes.c_uint32(0), _c_int64(-1)
+    _check("dg_get_debug_status", lib().dg_get_debug_status(ctypes.byref(flags), ctypes.byref(block), int(clear)))
+    return int(flags.value), int(block.value)
+
+
 _ws_cache = {}
+_ws_retired = []
 
 
 def default_workspace(device, nbytes):
-    """A zero-filled workspace per device, grown on demand (the kernels leave it zeroed)."""
-    key = torch.device(device).index
-    ws = _ws_cache.get(key)
+    """A zero-filled workspace for the current stream of `device`, grown on demand (the kernels
+    leave its counters zeroed).  Calls that share a workspace must be ordered on one stream, so
+    every (device, stream) pair gets its own.  A buffer that a larger request supersedes is kept
+    alive until the process ends, never freed: a graph captured with it, or a kernel still queued
+    on it, may use it later.  Inside graph capture there is no default workspace (a buffer made
+    there would be zero-filled only when the graph runs): pass one created before the capture."""
     if nbytes == 0:
         return None
+    dev = torch.device(device)
+    if dev.index is None:
+        dev = torch.device("cuda", torch.cuda.current_device())
+    stream = torch.cuda.current_stream(dev)
+    if torch.cuda.is_current_stream_capturing():
+        raise ValueError("no default workspace during graph capture: pass workspace= (a zero-filled uint8 "
+                         "tensor of dg_gemm_workspace_size(...) bytes created before the capture)")
+    key = (dev.index, stream.cuda_stream)
+    ws = _ws_cache.get(key)
     if ws is None or ws.numel() < nbytes:
-        ws = torch.zeros(max(nbytes, 1 << 20), dtype=torch.uint8, device=device)
+        if ws is not None:
+            _ws_retired.append(ws)
+        ws = torch.zeros(max(nbytes, 1 << 20), dtype=torch.uint8, device=dev)
         _ws_cache[key] = ws
     return ws
 

@@ -38,6 +38,7 @@ int launch_gemm_fq(const void* x, bool x_bf16, const uint8_t* b, const float* sb
 size_t gemm_fq_workspace_size(int64_t m, int64_t n, int64_t k, int num_cus);
 void gemm_config_name(int layout, int64_t m, int64_t n, int64_t k, int64_t groups, int num_cus, char* buf,
                       size_t len);
+int read_diag(unsigned out[4], bool clear);
 
 static thread_local char g_msg[512] = "";
 
@@ -46,8 +47,13 @@ int set_error(int status, const char* fmt, ...) {
   va_start(ap, fmt);
   vsnprintf(g_msg, sizeof(g_msg), fmt, ap);
   va_end(ap);
-  if (std::getenv("DG_DEBUG")) std::fprintf(stderr, "[dg] %s\n", g_msg);
+  if (debug_enabled()) std::fprintf(stderr, "[dg] %s\n", g_msg);
   return status;
+}
+
+bool debug_enabled() {
+  const char* v = std::getenv("DG_DEBUG");
+  return v != nullptr && v[0] != '\0' && !(v[0] == '0' && v[1] == '\0');
 }
 
 // ---- compute-unit cap (process-wide) ----------------------------------------
@@ -347,6 +353,16 @@ int dg_transpose_blocks(const uint8_t* q, const float* s, int64_t num_groups, in
   DG_REQUIRE(aligned16(q) && aligned16(qt), "transpose_blocks: code pointers must be 16-byte aligned");
   DG_REQUIRE(q != qt, "transpose_blocks: in-place transpose is not supported");
   return launch_transpose_blocks(q, s, num_groups, rows, cols, qt, st, static_cast<hipStream_t>(stream));
+}
+
+int dg_get_debug_status(uint32_t* flags, int64_t* block, int clear) {
+  DG_REQUIRE(flags != nullptr, "dg_get_debug_status: flags is null");
+  unsigned w[4] = {0u, 0u, 0u, 0u};
+  const int r = read_diag(w, clear != 0);
+  if (r != kOk) return r;
+  *flags = w[0];
+  if (block) *block = (int64_t)w[1] - 1;
+  return DG_OK;
 }
 
 const char* dg_gemm_config_name(int layout, int64_t m, int64_t n, int64_t k, int64_t num_groups) {

@@ -21,6 +21,10 @@ enum Status : int { kOk = 0, kInvalidArg = -1, kUnsupported = -2, kWorkspace = -
 // Records a thread-local error message (implemented in api.cpp).
 int set_error(int status, const char* fmt, ...);
 
+// DG_DEBUG set in the environment (read at every call): device-side layout checks and a log of
+// each GEMM's plan on stderr (implemented in api.cpp).
+bool debug_enabled();
+
 // Two fp32 -> two bf16, round to nearest even (a NaN stays a NaN, made quiet), packed little-endian
 // (lo in bits 0-15): one v_cvt_pk_bf16_f32.  On MI355X it equals the bit-level rounding
 // (u + 0x7fff + ((u >> 16) & 1)) >> 16 on every finite fp32 input, and (u >> 16) | 0x40 on NaNs

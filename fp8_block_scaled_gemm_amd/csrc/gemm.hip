@@ -45,6 +45,7 @@
 //    a separate quantizer launch costs in a HIP graph; the two-launch path stays the
 //    faster one.
 #include <cstdio>
+#include <cstdlib>
 #include <type_traits>
 
 #include "gemm_common.hpp"
@@ -63,6 +64,32 @@ __device__ __forceinline__ void lds_dma4(__amdgpu_buffer_rsrc_t rsrc, void* lds,
 }
 template <int V>
 using IC = std::integral_constant<int, V>;
+
+// Sticky diagnostics raised by the device code, one copy per device: word 0 holds DiagFlag bits,
+// word 1 the first 128-row block (+1) a contiguous-layout check found wrong.  Only atomics
+// write them; the host reads (and clears) them through read_diag after a synchronisation.
+__device__ unsigned g_diag[4];
+
+__device__ __forceinline__ void raise_diag(unsigned flag, unsigned detail_plus1) {
+  atomicOr(&g_diag[0], flag);
+  if (detail_plus1) atomicCAS(&g_diag[1], 0u, detail_plus1);
+}
+
+// DG_DEBUG check of one m-block of the contiguous layout: every row of a 128-row block must name
+// the expert of the block's first row, and that expert must be in [0, groups) - or the whole block
+// -1, the documented skip.  Reports through g_diag; the kernel goes on as without the check.
+template <int NT, int BM>
+__device__ __forceinline__ void check_contiguous_block(const int32_t* m_indices, int m, int groups, int m0) {
+  for (int i = threadIdx.x; i < BM; i += NT) {
+    const int row = m0 + i;
+    if (row >= m) break;
+    const int head = m_indices[row & ~(kGroup - 1)];
+    const int v = m_indices[row];
+    const unsigned blk = (unsigned)(row / kGroup) + 1u;
+    if (v != head) raise_diag(kDiagMixedBlock, blk);
+    else if ((v < 0 || v >= groups) && v != -1) raise_diag(kDiagExpertRange, blk);
+  }
+}
 
 template <int BN_, int BM_, int WN_, int WM_, int STAGES_, bool HALF_ISSUE_ = false>
 struct Cfg {
@@ -156,7 +183,7 @@ struct TileCoord {
 // inside a chunk and only a running workgroup takes one, so the wait ends however many of the
 // grid's workgroups are resident.
 constexpr int kFqGroupsPerLane = 4;   // groups per half-wave per chunk (loads in flight per lane)
-constexpr int kFqMaxPolls = 1 << 20;
+constexpr int kFqMaxPolls = 1 << 20;  // default bound of the wait (on the order of a second)
 
 template <int NT, class T>
 __device__ __forceinline__ void fq_chunk(const GemmParams& p, const T* x, int c, int groups,
@@ -224,13 +251,20 @@ __device__ __forceinline__ void fused_act_quant(const GemmParams& p, int* s_bcas
     had_chunk = true;
   }
   // Once every chunk is taken, the wait lasts about one chunk's time.  It gives up after
-  // kFqMaxPolls polls (on the order of a second) so that counters left non-zero by a misuse of
-  // the workspace give a wrong result instead of a wait that never ends.
-  if (tid == 0)
-    for (int poll = 0; poll < kFqMaxPolls; ++poll) {
-      if (__hip_atomic_load(done, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >= (unsigned)chunks) break;
+  // p.fq_max_polls polls (kFqMaxPolls: on the order of a second) so that counters left non-zero
+  // by a misuse of the workspace give a wrong result, flagged in the device diagnostics, instead
+  // of a wait that never ends.
+  if (tid == 0) {
+    bool finished = false;
+    for (int poll = 0; poll < p.fq_max_polls; ++poll) {
+      if (__hip_atomic_load(done, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >= (unsigned)chunks) {
+        finished = true;
+        break;
+      }
       __builtin_amdgcn_s_sleep(4);
     }
+    if (!finished) raise_diag(kDiagFqTimeout, 0u);   // the result of this call is not valid
+  }
   __syncthreads();
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
 }
@@ -335,6 +369,7 @@ __global__ __launch_bounds__(C::kThreads) void gemm_fp8_kernel(GemmParams p) {
     int expert = t.g;
     if constexpr (LAYOUT == kContiguous) {
       expert = p.m_indices[m0];
+      if (p.debug) check_contiguous_block<NT, C::BM>(p.m_indices, p.m, p.num_groups, m0);
       if (expert < 0 || expert >= p.num_groups) continue;   // uniform: skip unmapped block
     }
     const int kb_begin = split_item ? t.split * p.kb_per_split : 0;
@@ -925,7 +960,20 @@ static GemmParams make_params(int layout, const Plan& pl, const uint8_t* a, cons
   p.b_gstride = n * k;
   p.sb_gstride = (int64_t)p.nb128 * p.kb_total;
   p.d_gstride = m * n;
+  p.debug = debug_enabled() ? 1 : 0;
   return p;
+}
+
+// DG_DEBUG: one line per GEMM launch with the plan the host chose.
+static void log_plan(int layout, const Plan& pl, int64_t m, int64_t n, int64_t k, int64_t groups, size_t ws_bytes) {
+  static const char* const kNames[] = {"normal", "contiguous", "masked", "row-scaled"};
+  const LaunchInfo li = cfg_info<kDense>(pl.cfg);
+  std::fprintf(stderr,
+               "[dg] gemm %s m=%lld n=%lld k=%lld groups=%lld: %dx%d/%dwaves splits=%d%s kb_per_split=%d "
+               "tiles=%lld workspace=%zu/%zu bytes\n",
+               kNames[layout & 3], (long long)m, (long long)n, (long long)k, (long long)groups, li.bn, li.bm,
+               li.threads / 64, pl.splits, pl.tail_start > 0 ? " (last round only)" : "", pl.kb_per_split,
+               (long long)pl.tiles, pl.ws_bytes, ws_bytes);
 }
 
 int launch_gemm(int layout, const uint8_t* a, const float* sa, int64_t ld_sa, const uint8_t* b,
@@ -947,6 +995,7 @@ int launch_gemm(int layout, const uint8_t* a, const float* sa, int64_t ld_sa, co
     p.counters = static_cast<unsigned*>(ws);
     p.ws = reinterpret_cast<float*>(static_cast<uint8_t*>(ws) + kCounterBytes);
   }
+  if (p.debug) log_plan(layout, pl, m, n, k, groups, ws_bytes);
   switch (layout) {
     case kContiguous: return launch_layout<kContiguous>(p, pl, stream, num_cus);
     case kMasked: return launch_layout<kMasked>(p, pl, stream, num_cus);
@@ -998,6 +1047,13 @@ int launch_gemm_fq(const void* x, bool x_bf16, const uint8_t* b, const float* sb
   p.fq_x = x;
   p.fq_sync = static_cast<unsigned*>(ws) + kFqSyncWord;
   p.fq_bf16 = x_bf16 ? 1 : 0;
+  // DG_FQ_MAX_POLLS lowers the wait's bound (a test of the give-up path forces it from the host)
+  p.fq_max_polls = kFqMaxPolls;
+  if (const char* e = std::getenv("DG_FQ_MAX_POLLS")) {
+    const long v = std::strtol(e, nullptr, 10);
+    if (v >= 1 && v < kFqMaxPolls) p.fq_max_polls = (int)v;
+  }
+  if (p.debug) log_plan(kDense, f.pl, m, n, k, 1, ws_bytes);
   return launch_layout<kDense, true>(p, f.pl, stream, num_cus);
 }
 
@@ -1016,6 +1072,18 @@ int launch_fill_zero_bf16(uint16_t* d, int64_t count, hipStream_t stream) {
   hipLaunchKernelGGL(fill_zero_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, d, chunks);
   const hipError_t e = hipGetLastError();
   return e == hipSuccess ? kOk : set_error(kHip, "zero fill launch: %s", hipGetErrorString(e));
+}
+
+// The device diagnostics words of the current device, after every queued kernel on it has
+// finished; optionally cleared.
+int read_diag(unsigned out[4], bool clear) {
+  hipError_t e = hipDeviceSynchronize();
+  if (e == hipSuccess) e = hipMemcpyFromSymbol(out, HIP_SYMBOL(g_diag), 4 * sizeof(unsigned), 0, hipMemcpyDeviceToHost);
+  if (e == hipSuccess && clear) {
+    const unsigned zero[4] = {0u, 0u, 0u, 0u};
+    e = hipMemcpyToSymbol(HIP_SYMBOL(g_diag), zero, sizeof(zero), 0, hipMemcpyHostToDevice);
+  }
+  return e == hipSuccess ? kOk : set_error(kHip, "reading the device diagnostics: %s", hipGetErrorString(e));
 }
 
 }  // namespace dg

@@ -43,6 +43,16 @@ struct GemmParams {
   const void* fq_x;
   unsigned* fq_sync;
   int fq_bf16;
+  int fq_max_polls; // bound of the wait for every chunk (polls of the finished-chunk counter)
+  int debug;        // DG_DEBUG: run the layout checks and report through the diagnostics words
+};
+
+// Flag bits of the device diagnostics word (sticky until read with clearing).
+enum DiagFlag : unsigned {
+  kDiagMixedBlock = 1u,    // contiguous layout: a 128-row block whose rows name different experts
+  kDiagExpertRange = 2u,   // contiguous layout: an expert index outside [0, num_groups) other than a
+                           // whole block of -1
+  kDiagFqTimeout = 4u,     // in-launch activation quantization: the bounded wait gave up
 };
 
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));

@@ -322,6 +322,32 @@ size_t dg_gemm_workspace_size(int64_t m, int64_t n, int64_t k, int64_t num_group
  * per group), 3 row-scaled normal.  For profiling and reports; returns "" for invalid arguments. */
 const char* dg_gemm_config_name(int layout, int64_t m, int64_t n, int64_t k, int64_t num_groups);
 
+/*
+ * Debug facility (the analogue of the pages' debug switch among the environment variables,
+ * CSDN article, "environment variables").  With DG_DEBUG set to a value other than "" or "0"
+ * in the environment (read at every call):
+ *   - every GEMM launch logs its plan (tile configuration, K split, tiles, workspace) on stderr;
+ *   - the contiguous-grouped GEMM checks m_indices on the device: each 128-row block must carry
+ *     one expert index, in [0, num_groups) or -1 for the whole block.  A violation sets
+ *     DG_DIAG_MIXED_BLOCK or DG_DIAG_EXPERT_RANGE; the GEMM itself proceeds as without the check
+ *     (no trap, no fault: the rows of a mixed block are computed with the block's first expert).
+ * Independently of DG_DEBUG, the in-launch activation quantization sets DG_DIAG_FQ_TIMEOUT when
+ * its bounded wait gives up (a workspace whose counters were not zero): that call's output is
+ * not valid.
+ * The flags are sticky, one set per device, shared by every call on it.
+ */
+enum dg_diag_flag {
+  DG_DIAG_MIXED_BLOCK = 1,
+  DG_DIAG_EXPERT_RANGE = 2,
+  DG_DIAG_FQ_TIMEOUT = 4
+};
+
+/* Reads the diagnostics flags of the current device into *flags, and into *block (if not NULL)
+ * the index of the first 128-row block a contiguous-layout check found wrong (-1 if none).
+ * SYNCHRONISES the device first (a debugging call, not for the hot path).  clear != 0 resets
+ * the flags afterwards.  Returns DG_OK, DG_ERR_INVALID_ARG (flags NULL) or DG_ERR_HIP. */
+int dg_get_debug_status(uint32_t* flags, int64_t* block, int clear);
+
 #ifdef __cplusplus
 }
 #endif
