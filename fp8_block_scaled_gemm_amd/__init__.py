@@ -53,6 +53,8 @@ _SIGNATURES = {
     "dg_quantize_per_block": (ctypes.c_int, [_vp, _c_int64, _c_int64, _c_int64, _vp, _vp, _vp]),
     "dg_gemm_fp8_nt": (ctypes.c_int, [_vp, _vp, _c_int64, _vp, _vp, _vp, _c_int64, _c_int64, _c_int64,
                                       _vp, ctypes.c_size_t, _vp]),
+    "dg_gemm_fp8_nt_no_alloc": (ctypes.c_int, [_vp, _vp, _c_int64, _vp, _vp, _vp, _c_int64, _c_int64, _c_int64,
+                                               _vp]),
     "dg_gemm_fp8_nt_act_quant": (ctypes.c_int, [_vp, _vp, _vp, _vp, _c_int64, _c_int64, _c_int64, _vp,
                                                 ctypes.c_size_t, _vp]),
     "dg_gemm_fp8_nt_act_quant_bf16": (ctypes.c_int, [_vp, _vp, _vp, _vp, _c_int64, _c_int64, _c_int64, _vp,
@@ -320,6 +322,20 @@ def dg_gemm_fp8_nt(a, sa, b, sb, d=None, workspace=None, use_workspace=True):
     _check("dg_gemm_fp8_nt",
            lib().dg_gemm_fp8_nt(_ptr(a), _ptr(sa), sa.shape[-1], _ptr(b), _ptr(sb), _ptr(d), m, n, k,
                                 _ptr(workspace), ws_bytes, _stream(a)))
+    return d
+
+
+def dg_gemm_fp8_nt_no_alloc(a, sa, b, sb, d):
+    """dg_gemm_fp8_nt with the split-K scratch held by the library (no workspace argument; the
+    output d (M, N) bf16 must be given: this call allocates nothing)."""
+    a, b = _bytes(a), _bytes(b)
+    m, k = a.shape
+    n = b.shape[0]
+    _dev(a, sa, b, sb, d)
+    _require(d.dtype == torch.bfloat16 and tuple(d.shape) == (m, n), "d must be bfloat16 (M, N)")
+    _check("dg_gemm_fp8_nt_no_alloc",
+           lib().dg_gemm_fp8_nt_no_alloc(_ptr(a), _ptr(sa), sa.shape[-1], _ptr(b), _ptr(sb), _ptr(d), m, n, k,
+                                         _stream(a)))
     return d
 
 

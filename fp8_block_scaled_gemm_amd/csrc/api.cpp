@@ -39,6 +39,8 @@ size_t gemm_fq_workspace_size(int64_t m, int64_t n, int64_t k, int num_cus);
 void gemm_config_name(int layout, int64_t m, int64_t n, int64_t k, int64_t groups, int num_cus, char* buf,
                       size_t len);
 int read_diag(unsigned out[4], bool clear);
+int launch_gemm_no_alloc(const uint8_t* a, const float* sa, int64_t ld_sa, const uint8_t* b, const float* sb,
+                         uint16_t* d, int64_t m, int64_t n, int64_t k, hipStream_t stream, int num_cus);
 
 static thread_local char g_msg[512] = "";
 
@@ -192,6 +194,15 @@ int dg_gemm_fp8_nt(const uint8_t* a, const float* sa, int64_t ld_sa, const uint8
   if (cus < 0) return cus;
   return launch_gemm(0, a, sa, ld_sa, b, sb, 0, 0, d, nullptr, nullptr, 1, m, n, k, workspace,
                      workspace ? workspace_bytes : 0, static_cast<hipStream_t>(stream), cus);
+}
+
+int dg_gemm_fp8_nt_no_alloc(const uint8_t* a, const float* sa, int64_t ld_sa, const uint8_t* b, const float* sb,
+                            uint16_t* d, int64_t m, int64_t n, int64_t k, dg_stream_t stream) {
+  const int c = check_gemm_common(a, sa, ld_sa, b, sb, d, m, n, k);
+  if (c <= 0) return c;
+  const int cus = effective_cus();
+  if (cus < 0) return cus;
+  return launch_gemm_no_alloc(a, sa, ld_sa, b, sb, d, m, n, k, static_cast<hipStream_t>(stream), cus);
 }
 
 size_t dg_gemm_fp8_nt_act_quant_workspace_size(int64_t m, int64_t n, int64_t k) {

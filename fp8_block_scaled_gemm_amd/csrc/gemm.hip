@@ -46,6 +46,7 @@
 //    faster one.
 #include <cstdio>
 #include <cstdlib>
+#include <mutex>
 #include <type_traits>
 
 #include "gemm_common.hpp"
@@ -1072,6 +1073,51 @@ int launch_fill_zero_bf16(uint16_t* d, int64_t count, hipStream_t stream) {
   hipLaunchKernelGGL(fill_zero_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, d, chunks);
   const hipError_t e = hipGetLastError();
   return e == hipSuccess ? kOk : set_error(kHip, "zero fill launch: %s", hipGetErrorString(e));
+}
+
+// ---- normal GEMM that allocates nothing: split-K scratch in the library's own device array ------
+// For callers that cannot allocate (graph capture, tight serving loops): the split-K counters
+// and partials live in `scratch`, one copy per device, held until the process ends.  Host code
+// never passes the array's name to a kernel (on the host it is a stand-in, not a device address):
+// the device address comes from hipGetSymbolAddress once per device, with that device current.
+static __device__ __attribute__((aligned(256))) uint8_t scratch[kNoAllocScratchBytes];
+
+constexpr int kScratchDevices = 64;
+static std::mutex g_scratch_mu;
+static void* g_scratch_ptr[kScratchDevices];
+
+// The current device's scratch address; on the first call for a device also clears the counter
+// prefix (with a fill kernel on `stream`: no memset node if the caller is capturing a graph).
+static int scratch_for_device(void** out, hipStream_t stream) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return set_error(kHip, "no-alloc gemm: hipGetDevice: %s", hipGetErrorString(e));
+  if (dev < 0 || dev >= kScratchDevices) return set_error(kUnsupported, "no-alloc gemm: device %d", dev);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || ptr == nullptr)
+      return set_error(kHip, "no-alloc gemm: hipGetSymbolAddress(scratch): %s", hipGetErrorString(e));
+    const int r = launch_fill_zero_bf16(static_cast<uint16_t*>(ptr), (int64_t)(kCounterBytes / 2), stream);
+    if (r != kOk) return r;
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return kOk;
+}
+
+int launch_gemm_no_alloc(const uint8_t* a, const float* sa, int64_t ld_sa, const uint8_t* b, const float* sb,
+                         uint16_t* d, int64_t m, int64_t n, int64_t k, hipStream_t stream, int num_cus) {
+  const Plan pl = make_plan(kDense, m, n, k, 1, num_cus, true);
+  if (pl.ws_bytes > kNoAllocScratchBytes)
+    return set_error(kWorkspace, "no-alloc gemm: the plan %dx%d split %d needs %zu bytes of scratch, the library "
+                     "holds %zu", pl.bn, pl.bm, pl.splits, pl.ws_bytes, (size_t)kNoAllocScratchBytes);
+  void* ws = nullptr;
+  const int r = scratch_for_device(&ws, stream);
+  if (r != kOk) return r;
+  return launch_gemm(kDense, a, sa, ld_sa, b, sb, 0, 0, d, nullptr, nullptr, 1, m, n, k, ws, kNoAllocScratchBytes,
+                     stream, num_cus);
 }
 
 // The device diagnostics words of the current device, after every queued kernel on it has

@@ -128,4 +128,9 @@ constexpr size_t kCounterBytes = 64 * 1024;
 constexpr int64_t kFqSyncWord = kCounterBytes / 4 - 16;
 constexpr int64_t kMaxCounterTiles = kFqSyncWord;
 
+// Scratch the library holds per device for the normal GEMM that allocates nothing: the counter
+// prefix and the split-K partials of every plan of the DeepSeek-V3 shapes on 256 CUs (the largest,
+// 4096 x 7168 x 16384, needs ~41 MB).
+constexpr size_t kNoAllocScratchBytes = size_t(64) << 20;
+
 }  // namespace dg

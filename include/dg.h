@@ -171,6 +171,25 @@ int dg_gemm_fp8_nt_act_quant(const float* x, const uint8_t* b, const float* sb, 
 int dg_gemm_fp8_nt_act_quant_bf16(const uint16_t* x, const uint8_t* b, const float* sb, uint16_t* d, int64_t m,
                                   int64_t n, int64_t k, void* workspace, size_t workspace_bytes, dg_stream_t stream);
 
+/*
+ * The normal GEMM for callers that cannot allocate device memory: code under HIP graph capture,
+ * tight serving loops, harnesses that forbid allocation.  Same operation, arguments, layouts and
+ * result as dg_gemm_fp8_nt (the same tile plan and K split as with a large enough workspace, so
+ * the output is bit-identical to it), but the split-K counters and partials live in scratch
+ * memory the library holds itself: DG_NO_ALLOC_SCRATCH_BYTES of device memory per GPU it runs
+ * on, from the first call on that GPU until the process ends.  The call allocates nothing
+ * (no hipMalloc, no allocating library routine).
+ * Every call on one GPU shares that GPU's scratch: calls must be ordered on one stream (calls
+ * that overlap on one GPU race).  The counters are cleared on the first call on a GPU (a fill
+ * kernel on `stream`) and every call leaves them zero.
+ * Errors: as dg_gemm_fp8_nt, plus DG_ERR_WORKSPACE (before any launch) when the plan of the
+ * shape needs more scratch than DG_NO_ALLOC_SCRATCH_BYTES (no DeepSeek-V3 shape does on 256 CUs);
+ * DG_ERR_HIP if the scratch address cannot be obtained.
+ */
+#define DG_NO_ALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+int dg_gemm_fp8_nt_no_alloc(const uint8_t* a, const float* sa, int64_t ld_sa, const uint8_t* b, const float* sb,
+                            uint16_t* d, int64_t m, int64_t n, int64_t k, dg_stream_t stream);
+
 /* Workspace bytes dg_gemm_fp8_nt_act_quant(_bf16) needs for a shape (0 for invalid sizes). */
 size_t dg_gemm_fp8_nt_act_quant_workspace_size(int64_t m, int64_t n, int64_t k);
 
