@@ -1,8 +1,13 @@
 """Benchmark of the FP8 block-scaled GEMM hot path on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload dense_v3|small|contiguous|masked|
-                     large_dense|zipf|train_v3|train_moe|overlap] [--no-cpu-baseline] [--cpu-seconds S] [--eager]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload all|dense_v3|small|contiguous|masked|
+                     large_dense|zipf|train_v3|train_moe|overlap] [--no-flush] [--no-rotate]
+                     [--no-cpu-baseline] [--cpu-seconds S] [--eager]
     python bench.py --copy-calibration      # counter calibration: one plain 1 GiB device copy
+
+By default every configuration of the benchmark set runs (small, dense_v3, contiguous,
+masked, large_dense, zipf); dense_v3 - the DeepSeek-V3 dense shapes at M in {64, 128, 4096} -
+gives the headline fields, and every configuration gets its own entry under "configs".
 
 One step is one pass of the whole hot path over one batch of synthetic input:
 weight quantization (128x128 blocks) of every weight matrix of the workload,
@@ -10,12 +15,15 @@ then, per GEMM shape, activation quantization (1x128 groups) followed by the
 FP8 GEMM with promoted accumulation - every kernel of the library, in the order
 a forward pass runs them.  Inputs are resident in HBM before timing.
 
-Timing: the step is captured once as a HIP graph; the timed region is K graph
-replays on one stream, bracketed by device synchronisation (so microsecond
-kernels are not measured at the host's launch rate).  Per-kernel durations come
-from a second pass of K eager steps on the same stream with a HIP event pair
-around every launch; a bounded spin kernel ahead of each pass keeps the device
-busy while the host enqueues it, so every event pair brackets only its kernel.
+Timing, two passes per workload:
+  * the step: captured once as a HIP graph; the timed region is K graph replays on one
+    stream, bracketed by device synchronisation.  This gives `value` and `ms_per_step`.
+  * per launch: for each kernel of the step, an untimed 512 MB write first evicts the
+    256 MB last-level cache (MALL), then one HIP event pair on the launch stream brackets R
+    launches over R distinct copies of the weights (R copies > 768 MB, so no launch reads
+    weights another left in the cache); duration = time / R, median over K steps.  This is
+    the cold-weight duration a forward pass sees, and it amortises the event pair's own
+    few microseconds over R launches.  --no-flush / --no-rotate switch either off.
 
 Prints ONE JSON line: the workload's GEMM FP8 TFLOP/s over the whole step, plus
 per-shape GEMM TFLOP/s and HBM GB/s, the roofline of the dominant GEMM kernel
@@ -54,9 +62,12 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="dense_v3",
-                    choices=["dense_v3", "small", "contiguous", "masked", "large_dense", "zipf", "train_v3",
-                             "train_moe", "overlap"])
+    ap.add_argument("--workload", default="all",
+                    choices=["all", "dense_v3", "small", "contiguous", "masked", "large_dense", "zipf", "train_v3",
+                             "train_moe", "overlap"],
+                    help="all (default): every configuration of the benchmark set, dense_v3 as the headline")
+    ap.add_argument("--no-flush", action="store_true", help="no 512 MB write ahead of each timed GEMM")
+    ap.add_argument("--no-rotate", action="store_true", help="time each GEMM once per step, on its own weights")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target CPU work of the oracle sample")
     ap.add_argument("--eager", action="store_true", help="time eager launches instead of graph replays")
@@ -89,10 +100,16 @@ def Gen(torch, dev, seed):
 # ---------------------------------------------------------------------------
 
 class Op:
-    def __init__(self, kind, label, launch, flops=0.0, nbytes=0.0, config=""):
+    """One launch of the step.  A GEMM op may name its weight tensor (`weights`) and a function
+    launching it on any tensor of that shape (`make`): the per-kernel timing then runs it over
+    rotated copies of the weights, so that no launch finds its weights in the 256 MB MALL."""
+
+    def __init__(self, kind, label, launch, flops=0.0, nbytes=0.0, config="", weights=None, make=None):
         self.kind, self.label, self.launch = kind, label, launch
         self.flops, self.nbytes, self.config = float(flops), float(nbytes), config
-        self.times = []   # ms per timed step
+        self.weights, self.make = weights, make
+        self.copies = None
+        self.times = []   # ms per launch, one entry per timed step
 
 
 def dense_gemm_bytes(m, n, k):
@@ -156,11 +173,10 @@ def build_dense(torch, dg, dev, shapes, name, act_dtype="fp32", act_quant="separ
         ops.append(Op("aquant", f"aq {m}x{k}",
                       (lambda a32=a32, qa=qa, sa=sa: dg.dg_quantize_per_token_group(a32, q=qa, sa=sa)),
                       nbytes=quant_bytes(m * k, k, in_bytes)))
-        ops.append(Op("gemm", f"{m}x{n}x{k}",
-                      (lambda qa=qa, sa=sa, qb=qb, sb=sb, d=d, ws=ws: dg.dg_gemm_fp8_nt(qa, sa, qb, sb, d=d,
-                                                                                         workspace=ws)),
+        make = (lambda w, qa=qa, sa=sa, sb=sb, d=d, ws=ws: dg.dg_gemm_fp8_nt(qa, sa, w, sb, d=d, workspace=ws))
+        ops.append(Op("gemm", f"{m}x{n}x{k}", (lambda make=make, qb=qb: make(qb)),
                       flops=2.0 * m * n * k, nbytes=dense_gemm_bytes(m, n, k),
-                      config=dg.dg_gemm_config_name(0, m, n, k, 1)))
+                      config=dg.dg_gemm_config_name(0, m, n, k, 1), weights=qb, make=make))
     return ops
 
 
@@ -253,11 +269,12 @@ def build_contiguous(torch, dg, dev, cases):
                       nbytes=quant_bytes(m_total * k, k)))
         nbytes = (m_total * k + 4 * m_total * (k // 128) + g * (n * k + 4 * (-(-n // 128)) * (k // 128))
                   + 2 * m_total * n + 4 * m_total)
+        make = (lambda w, qa=qa, sa=sa, sb=sb, m_idx=m_idx, d=d:
+                dg.dg_gemm_fp8_grouped_contiguous(qa, sa, w, sb, m_idx, d=d))
         ops.append(Op("gemm", f"{label} G={g} rows={rows} (padded {m_total}) N={n} K={k}",
-                      (lambda qa=qa, sa=sa, qb=qb, sb=sb, m_idx=m_idx, d=d:
-                       dg.dg_gemm_fp8_grouped_contiguous(qa, sa, qb, sb, m_idx, d=d)),
+                      (lambda make=make, qb=qb: make(qb)),
                       flops=2.0 * rows * n * k, nbytes=nbytes,
-                      config=dg.dg_gemm_config_name(1, m_total, n, k, g)))
+                      config=dg.dg_gemm_config_name(1, m_total, n, k, g), weights=qb, make=make))
     return ops
 
 
@@ -356,11 +373,12 @@ def build_masked(torch, dg, dev, cases):
                       (lambda a32=a32, qa=qa, sa=sa: dg.dg_quantize_per_token_group(a32, q=qa, sa=sa)),
                       nbytes=quant_bytes(g * m_max * k, k)))
         nbytes = active * (n * k + 4 * (-(-n // 128)) * (k // 128)) + rows * (k + k // 32 + 2 * n) + 4 * g
+        make = (lambda w, qa=qa, sa=sa, sb=sb, d=d, masked=masked, ws=ws:
+                dg.dg_gemm_fp8_grouped_masked(qa, sa, w, sb, masked, d=d, workspace=ws))
         ops.append(Op("gemm", f"masked G={g} rows={rows} M_max={m_max} N={n} K={k}",
-                      (lambda qa=qa, sa=sa, qb=qb, sb=sb, d=d, masked=masked, ws=ws:
-                       dg.dg_gemm_fp8_grouped_masked(qa, sa, qb, sb, masked, d=d, workspace=ws)),
+                      (lambda make=make, qb=qb: make(qb)),
                       flops=2.0 * rows * n * k, nbytes=nbytes,
-                      config=dg.dg_gemm_config_name(2, m_max, n, k, g)))
+                      config=dg.dg_gemm_config_name(2, m_max, n, k, g), weights=qb, make=make))
     return ops
 
 
@@ -592,31 +610,53 @@ def copy_calibration(torch, dev, nbytes=1 << 30, reps=5):
     print(json.dumps({"copy_calibration_bytes": nbytes, "launches": reps}), flush=True)
 
 
-def main():
-    args = parse()
-    if args.gpus != 1:
-        print(f"bench.py: this build measures one GPU only (got --gpus {args.gpus}); the path has no "
-              "multi-GPU mode - see the sharding notes of the design document", file=sys.stderr)
-        sys.exit(2)
-    import torch
-    import fp8_block_scaled_gemm_amd as dg
+DEFAULT_SET = ["small", "dense_v3", "contiguous", "masked", "large_dense", "zipf"]
+HEADLINE = "dense_v3"
+ROT_BYTES = 768 << 20     # weight copies a GEMM's timed launches rotate over: > 3x the 256 MB MALL
+MAX_ROT = 32
+FLUSH_BYTES = 512 << 20   # untimed write ahead of every timed GEMM: the MALL holds none of its operands
 
-    if not torch.cuda.is_available():
-        print("bench.py: no GPU visible", file=sys.stderr)
-        sys.exit(1)
-    dev = torch.device("cuda", 0)
-    if args.copy_calibration:
-        copy_calibration(torch, dev)
-        return
-    dg.lib()
-    if args.num_cus > 0:
-        dg.dg_set_num_cus(args.num_cus)
-    if args.workload == "overlap":
-        overlap_bench(args, torch, dg, dev)
-        return
-    ops, desc = build_workload(args.workload, torch, dg, dev, args.act_dtype, args.act_quant)
+
+def kernel_of(config):
+    """Kernel instance of a GEMM configuration name (the K split is a launch parameter of the same
+    kernel): '256x192/8waves/split1' -> 'gemm_fp8_kernel 256x192/8waves'."""
+    return "gemm_fp8_kernel " + kernel_config(config)
+
+
+def rooflines(workload, ops):
+    """Per GEMM kernel instance of the step: its roofline against the bound its work sets (MFMA when
+    the flops take longer at peak than the bytes, else HBM), from the per-launch durations."""
+    by_k = {}
+    for op in ops:
+        if op.kind == "gemm":
+            by_k.setdefault(kernel_of(op.config), []).append(op)
+    out = {}
+    for kern, kops in by_k.items():
+        t = sum(sum(o.times) for o in kops) * 1e-3
+        launches = sum(len(o.times) for o in kops)
+        f = sum(o.flops * len(o.times) for o in kops)
+        b = sum(o.nbytes * len(o.times) for o in kops)
+        mfma = f / (PEAK_FP8_TFLOPS * 1e12) >= b / (PEAK_HBM_GBS * 1e9)
+        if mfma:
+            achieved, peak, unit = f / t / 1e12, PEAK_FP8_TFLOPS, "TFLOP/s"
+        else:
+            achieved, peak, unit = b / t / 1e9, PEAK_HBM_GBS, "GB/s"
+        traffic = measured_traffic(workload, kern, b / launches)
+        out[kern] = {"bound": "mfma" if mfma else "hbm", "achieved": round(achieved, 1), "peak": peak, "unit": unit,
+                     "frac": round(achieved / peak, 4),
+                     "traffic": traffic["bytes_per_launch"] if traffic else None, "traffic_detail": traffic,
+                     "kernel": kern, "launches": launches, "avg_launch_us": round(t / launches * 1e6, 2),
+                     "algorithmic_bytes_per_launch": round(b / launches), "flops_per_launch": round(f / launches),
+                     "device_us_per_step": round(t / max(1, len(kops[0].times)) * 1e6, 1),
+                     "shapes": sorted({o.label for o in kops})}
+    return out
+
+
+def run_workload(name, args, torch, dg, dev, stream, flush_buf):
+    """Build one workload, time its step (graph replays) and every launch (cold MALL), summarize."""
+    ops, desc = build_workload(name, torch, dg, dev, args.act_dtype, args.act_quant)
     torch.cuda.synchronize()
-    print(f"[bench] workload {args.workload}: {len(ops)} ops per step", file=sys.stderr, flush=True)
+    print(f"[bench] workload {name}: {len(ops)} ops per step", file=sys.stderr, flush=True)
 
     def step():
         for op in ops:
@@ -625,11 +665,9 @@ def main():
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    print("[bench] warmup done", file=sys.stderr, flush=True)
 
-    # ---- timed region: K steps, each one replay of the step captured as a HIP graph (no host
-    # launch gaps between the kernels); wall clock bracketed by device synchronisation --------------
-    stream = torch.cuda.Stream()
+    # ---- timed region: K steps, each one replay of the step captured as a HIP graph (no host launch
+    # gaps between the kernels); wall clock bracketed by device synchronisation ------------------------
     graph = None
     if not args.eager:
         graph = torch.cuda.CUDAGraph()
@@ -652,14 +690,21 @@ def main():
     t1 = time.perf_counter()
     ms_per_step = (t1 - t0) * 1e3 / args.steps
     gpu_ms_per_step = ev0.elapsed_time(ev1) / args.steps
-    print(f"[bench] timed {args.steps} steps: {ms_per_step:.3f} ms/step (device {gpu_ms_per_step:.3f})",
+    print(f"[bench] {name}: timed {args.steps} steps: {ms_per_step:.3f} ms/step (device {gpu_ms_per_step:.3f})",
           file=sys.stderr, flush=True)
+    del graph
 
-    # ---- per-kernel durations: the same step run eagerly on the same stream with a HIP event pair
-    # around every launch.  A bounded spin kernel first keeps the device busy while the host enqueues
-    # the whole step, so each event pair brackets only its kernel (no host gap), in step order. -------
-    n = len(ops)
-    # spin length: the counter rate of the spin kernel, measured
+    # ---- per-launch durations, cold MALL.  A GEMM runs R times back to back over R copies of its
+    # weights (R x weight bytes > 768 MB, so no launch finds its weights in the MALL) between one HIP
+    # event pair on the stream, after an untimed 512 MB write; its duration is the pair's time / R.
+    # Other launches (quantizers) take one event pair each.  A bounded spin kernel at the start of
+    # every step keeps the device busy while the host enqueues it. -----------------------------------
+    for op in ops:
+        if op.weights is not None and not args.no_rotate:
+            wbytes = op.weights.numel() * op.weights.element_size()
+            r = max(1, min(MAX_ROT, -(-ROT_BYTES // max(wbytes, 1))))
+            op.copies = [op.weights] + [op.weights.clone() for _ in range(r - 1)]
+    torch.cuda.synchronize()
     cal0, cal1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     with torch.cuda.stream(stream):
         torch.cuda._sleep(1_000_000)
@@ -669,63 +714,44 @@ def main():
     torch.cuda.synchronize()
     cycles_per_ms = 10_000_000 / max(cal0.elapsed_time(cal1), 1e-3)
     spin_cycles = int(args.spin_ms * cycles_per_ms)
+    n = len(ops)
     with torch.cuda.stream(stream):
         for _ in range(args.steps):
             ev = [torch.cuda.Event(enable_timing=True) for _ in range(2 * n)]
             torch.cuda._sleep(spin_cycles)
             for i, op in enumerate(ops):
+                if op.kind == "gemm" and flush_buf is not None:
+                    flush_buf.fill_(1)
                 ev[2 * i].record()
-                op.launch()
+                if op.copies:
+                    for w in op.copies:
+                        op.make(w)
+                else:
+                    op.launch()
                 ev[2 * i + 1].record()
             torch.cuda.synchronize()
             for i, op in enumerate(ops):
-                op.times.append(ev[2 * i].elapsed_time(ev[2 * i + 1]))
-    print("[bench] per-kernel timing done", file=sys.stderr, flush=True)
+                op.times.append(ev[2 * i].elapsed_time(ev[2 * i + 1]) / (len(op.copies) if op.copies else 1))
+    print(f"[bench] {name}: per-launch timing done", file=sys.stderr, flush=True)
+    for op in ops:
+        op.copies = None
 
     gemm_flops = sum(op.flops for op in ops if op.kind == "gemm")
-    value = gemm_flops / (ms_per_step * 1e-3) / 1e12
-
     shapes = []
     for op in ops:
         if op.kind != "gemm":
             continue
         t = float(np.median(op.times)) * 1e-3
-        tf = op.flops / t / 1e12
-        gb = op.nbytes / t / 1e9
+        tf, gb = op.flops / t / 1e12, op.nbytes / t / 1e9
+        rot = max(1, min(MAX_ROT, -(-ROT_BYTES // max(op.weights.numel(), 1)))) if op.weights is not None else 1
         shapes.append({"shape": op.label, "config": op.config, "us": round(t * 1e6, 2),
                        "tflops": round(tf, 1), "gbps": round(gb, 1),
                        "mfma_frac": round(tf / PEAK_FP8_TFLOPS, 4), "hbm_frac": round(gb / PEAK_HBM_GBS, 4),
                        "roofline_frac": round(max(op.flops / (PEAK_FP8_TFLOPS * 1e12),
-                                                  op.nbytes / (PEAK_HBM_GBS * 1e9)) / t, 4)})
-
-    # dominant GEMM kernel: the kernel instance (tile configuration; the K split is a launch
-    # parameter of the same kernel) with the most device time per step
-    by_cfg = {}
-    for op in ops:
-        if op.kind == "gemm":
-            by_cfg.setdefault(kernel_config(op.config), []).append(op)
-    dom_cfg, dom_ops = max(by_cfg.items(), key=lambda kv: sum(sum(o.times) for o in kv[1]))
-    tot_t = sum(sum(o.times) for o in dom_ops) * 1e-3
-    launches = sum(len(o.times) for o in dom_ops)
-    tot_f = sum(o.flops * len(o.times) for o in dom_ops)
-    tot_b = sum(o.nbytes * len(o.times) for o in dom_ops)
-    mfma_bound = tot_f / (PEAK_FP8_TFLOPS * 1e12) >= tot_b / (PEAK_HBM_GBS * 1e9)
-    if mfma_bound:
-        achieved, peak, unit = tot_f / tot_t / 1e12, PEAK_FP8_TFLOPS, "TFLOP/s"
-    else:
-        achieved, peak, unit = tot_b / tot_t / 1e9, PEAK_HBM_GBS, "GB/s"
-    kernel = f"gemm_fp8_kernel {dom_cfg}"
-    traffic = measured_traffic(args.workload, kernel, tot_b / launches)
-    roofline = {"bound": "mfma" if mfma_bound else "hbm", "achieved": round(achieved, 1), "peak": peak,
-                "unit": unit, "frac": round(achieved / peak, 4),
-                "traffic": traffic["bytes_per_launch"] if traffic else None,
-                "traffic_detail": traffic,
-                "kernel": kernel, "launches": launches,
-                "avg_launch_us": round(tot_t / launches * 1e6, 2),
-                "algorithmic_bytes_per_launch": round(tot_b / launches),
-                "flops_per_launch": round(tot_f / launches),
-                "shapes": sorted({o.label for o in dom_ops})}
-
+                                                  op.nbytes / (PEAK_HBM_GBS * 1e9)) / t, 4),
+                       "rotations": 1 if args.no_rotate else rot})
+    kernels = rooflines(name, ops)
+    dominant = max(kernels.values(), key=lambda r: r["avg_launch_us"] * r["launches"])
     quant = {}
     for kind in ("wquant", "aquant", "cquant", "transpose"):
         ks = [op for op in ops if op.kind == kind]
@@ -735,30 +761,74 @@ def main():
             quant[kind] = {"us": round(t * 1e6, 1), "gbps": round(b / t / 1e9, 1),
                            "hbm_frac": round(b / t / 1e9 / PEAK_HBM_GBS, 4)}
     gemm_only_ms = sum(float(np.median(o.times)) for o in ops if o.kind == "gemm")
+    summary = {"workload": name, "description": desc,
+               "value": round(gemm_flops / (ms_per_step * 1e-3) / 1e12, 2), "unit": "TFLOP/s",
+               "ms_per_step": round(ms_per_step, 4), "device_ms_per_step": round(gpu_ms_per_step, 4),
+               "gemms": len(shapes), "gemm_only_ms": round(gemm_only_ms, 4),
+               "gemm_only_tflops": round(gemm_flops / (gemm_only_ms * 1e-3) / 1e12, 1),
+               "timing": "eager" if args.eager else "hip graph replay per step",
+               "roofline": dominant, "kernels": kernels, "quant": quant, "shapes": shapes}
+    del ops
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    return summary
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py: this build measures one GPU only (got --gpus {args.gpus}); the path has no "
+              "multi-GPU mode - see the sharding notes of the design document", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import fp8_block_scaled_gemm_amd as dg
+
+    if not torch.cuda.is_available():
+        print("bench.py: no GPU visible", file=sys.stderr)
+        sys.exit(1)
+    dev = torch.device("cuda", 0)
+    if args.copy_calibration:
+        copy_calibration(torch, dev)
+        return
+    dg.lib()
+    if args.num_cus > 0:
+        dg.dg_set_num_cus(args.num_cus)
+    if args.workload == "overlap":
+        overlap_bench(args, torch, dg, dev)
+        return
+    names = DEFAULT_SET if args.workload == "all" else [args.workload]
+    stream = torch.cuda.Stream()
+    flush_buf = None if args.no_flush else torch.empty(FLUSH_BYTES, dtype=torch.uint8, device=dev)
+    results = {}
+    for name in names:
+        results[name] = run_workload(name, args, torch, dg, dev, stream, flush_buf)
+    head = results[HEADLINE] if HEADLINE in results else results[names[0]]
 
     cpu = None
     if not args.no_cpu_baseline:
         print("[bench] cpu baseline ...", file=sys.stderr, flush=True)
-        cpu = cpu_baseline(args.workload, args.cpu_seconds)
+        cpu = cpu_baseline(head["workload"], args.cpu_seconds)
 
-    out = {"metric": METRIC, "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
-           "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4), "higher_is_better": True,
+    config = {"workload": head["workload"], "description": head["description"], "gemms": head["gemms"],
+              "activation_input": args.act_dtype, "activation_quantization": args.act_quant,
+              "step": ("per (N,K): weight quantization + transpose; forward (quantize X, GEMM), dgrad "
+                       "(quantize dY, GEMM with W^T), wgrad (per-channel quantize dY and X, row-scaled GEMM)"
+                       if head["workload"] == "train_v3" else
+                       "per (N,K): expert weight quantization + transpose; forward (quantize X, contiguous GEMM), "
+                       "dgrad (quantize dY, contiguous GEMM with W_e^T), wgrad (per-channel quantize dY and X, "
+                       "k-grouped row-scaled GEMM)" if head["workload"] == "train_moe" else
+                       "weight quantization (all weights) + per shape: activation quantization, FP8 GEMM"),
+              "timing": head["timing"], "device_ms_per_step": head["device_ms_per_step"],
+              "gemm_only_tflops": head["gemm_only_tflops"], "gemm_only_ms": head["gemm_only_ms"],
+              "per_launch_timing": ("median over steps; each GEMM after an untimed 512 MB write, launched over "
+                                    "rotated weight copies (> 768 MB) between one event pair, time / copies"),
+              "also_timed": [n for n in names if n != head["workload"]]}
+    out = {"metric": METRIC, "value": head["value"], "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+           "warmup": args.warmup, "ms_per_step": head["ms_per_step"], "higher_is_better": True,
            "scaling": "weak", "vs_baseline": None, "dtype": "fp8_e4m3", "data": "synthetic",
-           "config": {"workload": args.workload, "description": desc, "gemms": len(shapes),
-                      "activation_input": args.act_dtype,
-                      "activation_quantization": args.act_quant,
-                      "step": ("per (N,K): weight quantization + transpose; forward (quantize X, GEMM), dgrad "
-                               "(quantize dY, GEMM with W^T), wgrad (per-channel quantize dY and X, row-scaled GEMM)"
-                               if args.workload == "train_v3" else
-                               "per (N,K): expert weight quantization + transpose; forward (quantize X, contiguous GEMM), "
-                               "dgrad (quantize dY, contiguous GEMM with W_e^T), wgrad (per-channel quantize dY and X, "
-                               "k-grouped row-scaled GEMM)" if args.workload == "train_moe" else
-                               "weight quantization (all weights) + per shape: activation quantization, FP8 GEMM"),
-                      "timing": "eager" if graph is None else "hip graph replay per step",
-                      "device_ms_per_step": round(gpu_ms_per_step, 4),
-                      "gemm_only_tflops": round(gemm_flops / (gemm_only_ms * 1e-3) / 1e12, 1),
-                      "gemm_only_ms": round(gemm_only_ms, 4)},
-           "roofline": roofline, "cpu_baseline": cpu, "quant": quant, "shapes": shapes}
+           "config": config, "roofline": head["roofline"], "cpu_baseline": cpu, "quant": head["quant"],
+           "shapes": head["shapes"],
+           "configs": {n: {k: v for k, v in r.items() if k != "description"} for n, r in results.items()}}
     print(json.dumps(out), flush=True)
 
 
