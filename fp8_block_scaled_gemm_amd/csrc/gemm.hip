@@ -92,9 +92,12 @@ __device__ __forceinline__ void check_contiguous_block(const int32_t* m_indices,
   }
 }
 
-template <int BN_, int BM_, int WN_, int WM_, int STAGES_, bool HALF_ISSUE_ = false>
+template <int BN_, int BM_, int WN_, int WM_, int STAGES_, bool HALF_ISSUE_ = false, bool PIPE_ = false>
 struct Cfg {
   static constexpr int BN = BN_, BM = BM_, WN = WN_, WM = WM_, STAGES = STAGES_;
+  // PIPE: the two-slot main loop that overlaps every K block's operand reads and DMA issue with
+  // the previous block's MFMAs (one barrier per K block, placed two fragment rows before its end)
+  static constexpr bool PIPE = PIPE_;
   static constexpr int kWavesN = BN / WN;
   static constexpr int kWavesM = BM / WM;
   static constexpr int kWaves = kWavesN * kWavesM;
@@ -119,11 +122,16 @@ struct Cfg {
   static constexpr int kSaLanesPerWave = (BM / 4 + kIssuers - 1) / kIssuers;
   // vector-memory instructions an issuing thread issues per stage: operand DMAs + the two scale DMAs
   static constexpr int kVmPerStage = kDmaPerWave + 2;
+  // PIPE stage: the operand tiles, then per wave 64 activation scales (256 B) and, after all of
+  // those, per wave 64 copies of its weight block's scale (256 B)
+  static constexpr int kPipeSaOffset = (BN + BM) * kGroup;
+  static constexpr int kPipeSbOffset = kPipeSaOffset + kWaves * 256;
   static_assert(kDma % kIssuers == 0 && kDmaB % kIssuers == 0, "DMA instructions must split evenly over waves");
   static_assert(kIssuers % 2 == 0, "a DMA band must span a multiple of 16 rows (the swizzle period)");
   static_assert(WN % 16 == 0 && WM % 16 == 0 && 128 % WN == 0, "wave tile must be 16-aligned, WN | 128");
   static_assert(STAGES >= 2 && STAGES <= 4, "2..4 stages");
   static_assert(kVmPerStage * (STAGES - 1) < 64, "vmcnt range");
+  static_assert(!PIPE || (STAGES == 2 && WN / 16 >= 3 && !HALF_ISSUE_), "PIPE: two slots, >= 3 fragment rows, all waves issue");
   // every issuing wave issues exactly kVmPerStage instructions per stage (lane 0 of each scale DMA
   // is active), which the vmcnt waits count on
   static_assert(kSaLanesPerWave <= 64 && BM % 4 == 0 && (kIssuers - 1) * kSaLanesPerWave < BM / 4,
@@ -136,6 +144,7 @@ struct Cfg {
 // copies of the tile's block scales, or BN per-row scales for kDenseRowB).
 template <class C, int LAYOUT>
 constexpr int stage_bytes() {
+  if constexpr (C::PIPE) return C::kPipeSbOffset + C::kWaves * 256;
   return C::kSbOffset + (LAYOUT == kDenseRowB ? C::BN * 4 : C::kIssuers * C::kSbWaveBytes);
 }
 
@@ -544,7 +553,198 @@ __global__ __launch_bounds__(C::kThreads) void gemm_fp8_kernel(GemmParams p) {
       }
     };
 
-    // ---- main loop: ring of S stages, one barrier per K block -------------------
+    // ---- main loop ---------------------------------------------------------------
+    if constexpr (C::PIPE) {
+      // Two slots; a K block's operands come from slot tk & 1.  A wave's A fragments (weight rows)
+      // are read two fragment rows ahead of their MFMAs, its B fragments (activation rows) and
+      // scales one block ahead: every LDS read has two rows of MFMAs to return, the block
+      // boundaries included.  Two rows before the end of block tk every wave has read all it reads
+      // of slot tk & 1 and waits for its own DMAs of block tk+1; one barrier then makes both hold
+      // for every wave.  After it, block tk+2's DMAs go into slot tk & 1, and block tk+1's scales,
+      // first two A fragments and (each as soon as the last row's MFMA has consumed its
+      // predecessor) B fragments are read from the other slot while the last two rows of block tk
+      // run.  Every DMA of a block thus has one block's compute to land.  The block body has no
+      // branch (a branch there lets the compiler sink the MFMAs below the barrier): past the last
+      // K block the DMAs take out-of-range offsets and write zeros that nothing reads, and the
+      // scales come by two all-lane DMAs per wave into the wave's own copy.
+      static_assert(!kRowB, "per-row B scales run on the three-stage loop");
+      constexpr int kFN = C::kFragN, kFM = C::kFragM;
+      constexpr int kBarRow = kFN - 2;   // the rows after the barrier: kBarRow and the last one
+      static_assert(kBarRow >= 1, "PIPE: at least three fragment rows");
+      constexpr uint32_t kOut = 0xFFFFFFF0u;   // an offset past every resource: the DMA writes zeros
+      using SlotPtr = const uint8_t*;
+      const int lane_off = lds_off(l16, 2 * g4);
+      // this wave's activation-scale rows m0 + wm0 + lane (64 of them, the wave's WM first) and the
+      // scale of its weight block, as byte offsets within a K block's scale row
+      const int sa_row = m0 + wm0 + lane;
+      const uint32_t sa_lane_off = sa_row < (int)p.ld_sa ? (uint32_t)sa_row * 4u : kOut;
+      int sb_blk_w = (n0 + wn0) >> 7;
+      sb_blk_w = sb_blk_w < p.nb128 ? sb_blk_w : p.nb128 - 1;
+      const uint32_t sb_wave_off = (uint32_t)sb_blk_w * (uint32_t)p.kb_total * 4u;
+      // The DMAs of one stage, issued one at a time (DMA d < kDmaPerWave: operand rows; then the
+      // activation scales and the weight-block scale), so that the issue can be spread over MFMAs.
+      constexpr int kStageDmas = C::kDmaPerWave + 2;
+      struct DmaCtx {
+        uint8_t* sbase;
+        int kb;
+        uint32_t base_off, out_mask, inv_mask;
+      };
+      auto dma_ctx = [&](int tk, auto slot_c, bool valid) {
+        constexpr int slot = decltype(slot_c)::value;
+        DmaCtx c;
+        c.sbase = slot == 0 ? st0 : st1;
+        c.kb = kb_begin + tk;
+        c.base_off = dma_off;
+        asm volatile("" : "+v"(c.base_off));
+        // bitwise, not short-circuit: a branch here would split the block body
+        const uint32_t out = (uint32_t)(!valid) | ((uint32_t)((c.kb + 1) * kGroup > p.k) &
+                                                   (uint32_t)(c.kb * kGroup + dma_chunk >= p.k));
+        c.out_mask = 0u - out;                   // all ones: out of range
+        c.inv_mask = 0u - (uint32_t)(!valid);
+        return c;
+      };
+      auto dma_one = [&](const DmaCtx& c, int d) {
+        if (d < C::kDmaPerWave) {
+          const int q = iw + C::kIssuers * d;
+          const bool is_b = d < kBandsB;
+          const uint32_t voff = c.base_off + (uint32_t)(is_b ? d : d - kBandsB) * band_step;
+          lds_dma16(is_b ? rs_b : rs_a, c.sbase + q * (C::kDmaRows * kGroup), voff | (c.out_mask & kOut),
+                    c.kb * kGroup);
+        } else if (d == C::kDmaPerWave) {
+          // (readfirstlane: the offset is uniform; keeps the compiler from computing it per lane)
+          lds_dma4(rs_sa, c.sbase + C::kPipeSaOffset + wave * 256, sa_lane_off | (c.inv_mask & kOut),
+                   __builtin_amdgcn_readfirstlane(c.kb * (int)p.ld_sa * 4));
+        } else {
+          lds_dma4(rs_sb, c.sbase + C::kPipeSbOffset + wave * 256, sb_wave_off | (c.inv_mask & kOut),
+                   __builtin_amdgcn_readfirstlane(c.kb * 4));
+        }
+      };
+      auto issue_pipe = [&](int tk, auto slot_c, bool valid) {
+        const DmaCtx c = dma_ctx(tk, slot_c, valid);
+#pragma unroll
+        for (int d = 0; d < kStageDmas; ++d) dma_one(c, d);
+      };
+      auto read_a = [&](SlotPtr sbase, int i) {
+        const int off = (wn0 + 16 * i) * kGroup + lane_off;
+        return make_v8i(*reinterpret_cast<const u32x4*>(sbase + off),
+                        *reinterpret_cast<const u32x4*>(sbase + (off ^ 16)));
+      };
+      auto read_b = [&](SlotPtr sbase, int j) {
+        const int off = (C::BN + wm0 + 16 * j) * kGroup + lane_off;
+        return make_v8i(*reinterpret_cast<const u32x4*>(sbase + off),
+                        *reinterpret_cast<const u32x4*>(sbase + (off ^ 16)));
+      };
+      // the scales of the block in slot sbase: the lane's activation scale of each B fragment in
+      // raw[0, kFM), the wave's weight-block scale in raw[kFM] (multiplied where first used, so
+      // that nothing waits for these reads)
+      auto read_scales = [&](SlotPtr sbase, float* raw) {
+        const float* sa_w = reinterpret_cast<const float*>(sbase + C::kPipeSaOffset + wave * 256);
+#pragma unroll
+        for (int j = 0; j < kFM; ++j) raw[j] = sa_w[16 * j + l16];
+        raw[kFM] = *reinterpret_cast<const float*>(sbase + C::kPipeSbOffset + wave * 256);
+      };
+      // Fragment rows [R0, R1) of the block in slot cur; the rows from 0 first form the promotion
+      // scales sc[j] = fl32(sa * sb) from the raw ones.  Row i takes its A fragment from a[i % 3]
+      // and, at its start, requests row i+2's (rows kFN and kFN+1 are the next block's rows 0 and
+      // 1, from slot nxt: only the rows after the barrier reach them).  In the last row, B fragment
+      // j is replaced by the next block's as soon as that row's MFMA j has been issued.  The
+      // promotion FMAs run one MFMA behind (flushed at the end).  Rows ahead of a barrier pin their
+      // accumulators at the end, so that no MFMA of theirs can move below it.
+      auto rows = [&](auto r0_c, auto r1_c, SlotPtr cur, SlotPtr nxt, v8i* a, v8i* bop, float* sc, const float* raw,
+                      const DmaCtx* dc) {
+        constexpr int R0 = decltype(r0_c)::value, R1 = decltype(r1_c)::value;
+        if constexpr (R0 == 0) {
+#pragma unroll
+          for (int j = 0; j < kFM; ++j) sc[j] = raw[j] * raw[kFM];   // fl32(sa * sb)
+        }
+        constexpr int T = (R1 - R0) * kFM;   // MFMAs of these rows; with dc, the stage's DMAs spread over them
+        v4f part[2];
+#pragma unroll
+        for (int q = R0 * kFM; q <= R1 * kFM; ++q) {
+          if (q < R1 * kFM) {
+            const int i = q / kFM, j = q % kFM;
+            if (j == 0) {
+              __builtin_amdgcn_sched_barrier(0);
+              const int r = i + 2;
+              a[r % 3] = r < kFN ? read_a(cur, r) : read_a(nxt, r - kFN);
+            }
+            part[q & 1] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+                a[i % 3], bop[j], v4f{0.f, 0.f, 0.f, 0.f}, 0, 0, 0, 127, 0, 127);
+            if (i == kFN - 1) bop[j] = read_b(nxt, j);
+          }
+          if (q > R0 * kFM) {
+            const int i = (q - 1) / kFM, j = (q - 1) % kFM;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) acc[i][j][r] = __builtin_fmaf(part[(q - 1) & 1][r], sc[j], acc[i][j][r]);
+          }
+          if (q > R0 * kFM && q < R1 * kFM) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA of q
+            __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);   // FMAs of q-1
+          }
+          if (dc != nullptr && q < R1 * kFM) {
+            // after MFMA t of these rows: DMAs [t * D / T, (t + 1) * D / T)
+            const int t = q - R0 * kFM;
+            const int d0 = t * kStageDmas / T, d1 = (t + 1) * kStageDmas / T;
+            for (int d = d0; d < d1; ++d) dma_one(*dc, d);
+          }
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        if constexpr (R1 == kBarRow) {
+#pragma unroll
+          for (int q = R0 * kFM; q < R1 * kFM; ++q) asm volatile("" : "+v"(acc[q / kFM][q % kFM]));
+        }
+      };
+      // The barrier of block tk (slot CUR; the next block in slot NXT) and its last two rows.  A
+      // loop iteration starts here: it waits for every DMA in flight, so what the compiler's wait
+      // insertion cannot track across the loop's back edge costs nothing.  On return a[0], a[1]
+      // hold the next block's first two A fragments, bop its B fragments, rn its raw scales.
+      auto bar_tail = [&](int tk, auto cur_c, auto nxt_c, v8i* a, v8i* bop, float* sc, float* rn) {
+        constexpr int cur_slot = decltype(cur_c)::value;
+        constexpr int nxt_slot = decltype(nxt_c)::value;
+        const SlotPtr cur = cur_slot == 0 ? st0 : st1;
+        const SlotPtr nxt = nxt_slot == 0 ? st0 : st1;
+        __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0): this wave's reads of slot CUR are done
+        wait_vmcnt<0>();                      // its DMAs of block tk+1 have landed
+        __syncthreads();                      // ... and every wave's
+        const DmaCtx dc = dma_ctx(tk + 2, cur_c, tk + 2 < nk);
+        read_scales(nxt, rn);
+        rows(IC<kBarRow>{}, IC<kFN>{}, cur, nxt, a, bop, sc, nullptr, &dc);
+        const v8i n0a = a[kFN % 3], n1a = a[(kFN + 1) % 3];
+        a[0] = n0a;
+        a[1] = n1a;
+      };
+      wait_vmcnt<0>();
+      __syncthreads();   // the previous tile's readers are done with both slots
+      if (nk > 0) {      // (k = 0: no K block, the accumulators stay zero)
+      issue_pipe(0, IC<0>{}, true);
+      wait_vmcnt<0>();
+      __syncthreads();   // block 0 landed for every wave
+      issue_pipe(1, IC<1>{}, nk > 1);
+      v8i bop[kFM], a[3];
+      float sc[kFM], r0[kFM + 1], r1[kFM + 1];
+#pragma unroll
+      for (int j = 0; j < kFM; ++j) bop[j] = read_b(st0, j);
+      read_scales(st0, r0);
+      a[0] = read_a(st0, 0);
+      a[1] = read_a(st0, 1);
+      // block 0 up to its barrier row
+      rows(IC<0>{}, IC<kBarRow>{}, st0, st1, a, bop, sc, r0, nullptr);
+      // two blocks per iteration (the slots alternate), while a block tk+2 follows; then the rest
+      int tk = 0;
+      for (; tk + 2 < nk; tk += 2) {
+        bar_tail(tk, IC<0>{}, IC<1>{}, a, bop, sc, r1);
+        rows(IC<0>{}, IC<kBarRow>{}, st1, st0, a, bop, sc, r1, nullptr);
+        bar_tail(tk + 1, IC<1>{}, IC<0>{}, a, bop, sc, r0);
+        rows(IC<0>{}, IC<kBarRow>{}, st0, st1, a, bop, sc, r0, nullptr);
+      }
+      bar_tail(tk, IC<0>{}, IC<1>{}, a, bop, sc, r1);
+      if (tk + 1 < nk) {
+        rows(IC<0>{}, IC<kBarRow>{}, st1, st0, a, bop, sc, r1, nullptr);
+        bar_tail(tk + 1, IC<1>{}, IC<0>{}, a, bop, sc, r0);
+      }
+      wait_vmcnt<0>();   // the zero-filling DMAs past the last K block
+      }
+    } else {
     __syncthreads();   // the previous tile's readers are done with every stage
 #pragma unroll
     for (int s = 0; s < S - 1; ++s)
@@ -565,6 +765,7 @@ __global__ __launch_bounds__(C::kThreads) void gemm_fp8_kernel(GemmParams p) {
         else if (s == 2) compute(IC<(S > 2 ? 2 : 0)>{});
         else compute(IC<(S > 3 ? 3 : 0)>{});
       }
+    }
     }
 
     // ---- split-K: last arriving workgroup sums partials in split order ---------
@@ -595,24 +796,32 @@ __global__ __launch_bounds__(C::kThreads) void gemm_fp8_kernel(GemmParams p) {
       if (!s_flag) continue;
       // fixed order acc = p_0 + p_1 + ... + p_{S-1}, every partial (this workgroup's own
       // included) read back from the workspace, so the sum does not depend on who arrived last.
-      // Up to kBatch splits are loaded together (all in flight) before they are added.
+      // Up to kBatch splits of kChunk fragments are loaded together (all in flight) before they are
+      // added (at most 32 fragments' worth of registers; 16 on tiles whose accumulators take 128).
+      constexpr int kChunk = kFrags >= 32 ? 16 : kFrags;
       constexpr int kBatch = kFrags >= 32 ? 1 : 32 / kFrags;
-      for (int s0 = 0; s0 < p.splits; s0 += kBatch) {
-        v4f v[kBatch][kFrags];
+      static_assert(kFrags % kChunk == 0, "fragment chunks");
 #pragma unroll
-        for (int u = 0; u < kBatch; ++u) {
-          const int sp = s0 + u < p.splits ? s0 + u : s0;
+      for (int f0 = 0; f0 < kFrags; f0 += kChunk) {
+        for (int s0 = 0; s0 < p.splits; s0 += kBatch) {
+          v4f v[kBatch][kChunk];
 #pragma unroll
-          for (int f = 0; f < kFrags; ++f)
-            v[u][f] = __builtin_bit_cast(v4f, __builtin_amdgcn_raw_buffer_load_b128(
-                                                  rs_ws, sp * kSplitBytes + tid * 16 + f * NT * 16, 0, kCpolSc1));
-        }
+          for (int u = 0; u < kBatch; ++u) {
+            const int sp = s0 + u < p.splits ? s0 + u : s0;
 #pragma unroll
-        for (int u = 0; u < kBatch; ++u) {
-          if (s0 + u >= p.splits) break;
+            for (int f = 0; f < kChunk; ++f)
+              v[u][f] = __builtin_bit_cast(v4f, __builtin_amdgcn_raw_buffer_load_b128(
+                                                    rs_ws, sp * kSplitBytes + tid * 16 + (f0 + f) * NT * 16, 0, kCpolSc1));
+          }
 #pragma unroll
-          for (int f = 0; f < kFrags; ++f)
-            acc[f / C::kFragM][f % C::kFragM] = (s0 + u == 0) ? v[u][f] : acc[f / C::kFragM][f % C::kFragM] + v[u][f];
+          for (int u = 0; u < kBatch; ++u) {
+            if (s0 + u >= p.splits) break;
+#pragma unroll
+            for (int f = 0; f < kChunk; ++f) {
+              v4f& dst = acc[(f0 + f) / C::kFragM][(f0 + f) % C::kFragM];
+              dst = (s0 + u == 0) ? v[u][f] : dst + v[u][f];
+            }
+          }
         }
       }
       if (tid == 0)   // leave the counter zeroed for the next call
@@ -707,19 +916,24 @@ static LaunchInfo info() {
 
 // Tile configurations: BN x BM workgroup tile, WN x WM wave tile, LDS stages.
 //  kCfgLarge   256x128, 8 waves of 64x64, 3 stages (~147 KB LDS): compute-bound shapes.
-//  kCfgRows128 the same tile for the contiguous layout (the expert changes every 128 rows).
-//  kCfgWide    256x192, 8 waves of 128x48, 2 stages (~114 KB LDS): 1.5x the work per tile and
-//              ~1/6 less operand traffic per flop than kCfgLarge; chosen when it needs fewer
-//              rounds of the persistent grid (wave quantisation decides most shapes).
+//  kCfgRows128 256x128 for the contiguous layout (the expert changes every 128 rows, so no tile
+//              spans more): 8 waves of 64x64, two slots (~104 KB LDS), the pipelined main loop.
+//  kCfgWide    256x192, 8 waves of 128x48, two slots (~120 KB LDS), the pipelined main loop: 1.5x
+//              the work per tile and ~1/6 less operand traffic per flop than kCfgLarge.
+//  kCfgSquare  256x256, 8 waves of 128x64, two slots (~136 KB LDS), the pipelined main loop: 2x the
+//              work per tile, 1/4 less operand traffic per flop than kCfgLarge and 1/6 fewer LDS
+//              reads per MFMA than kCfgWide.  The planner picks whichever of the three needs the
+//              least time in rounds of the persistent grid (wave quantisation decides most shapes).
 //  kCfgDec*    m <= 128 rows: 64 weight rows x 64 or 128 activation rows, 4 waves, two
 //              workgroups per CU: HBM-bound shapes (for 65..128 rows the planner's model picks
 //              one 128-row or two 64-row activation tiles).  (Measured against 128-row weight
 //              tiles on all twelve M = 64 / 128 DeepSeek-V3 shapes: the 64-row weight tile, with
 //              K split to fill the grid, is faster on every one.)
-enum CfgId : int { kCfgLarge = 0, kCfgRows128, kCfgWide, kCfgDec64, kCfgDec128, kNumCfg };
+enum CfgId : int { kCfgLarge = 0, kCfgRows128, kCfgWide, kCfgDec64, kCfgDec128, kCfgSquare, kNumCfg };
 using CfgLarge = Cfg<256, 128, 64, 64, 3, true>;
-using CfgRows128 = Cfg<256, 128, 64, 64, 3, true>;
-using CfgWide = Cfg<256, 192, 128, 48, 2, true>;
+using CfgRows128 = Cfg<256, 128, 64, 64, 2, false, true>;
+using CfgWide = Cfg<256, 192, 128, 48, 2, false, true>;
+using CfgSquare = Cfg<256, 256, 128, 64, 2, false, true>;
 using CfgDec64 = Cfg<64, 64, 32, 32, 4>;
 using CfgDec128 = Cfg<64, 128, 32, 64, 3>;
 
@@ -731,10 +945,13 @@ static LaunchInfo cfg_info(int cfg) {
     case kCfgWide:
       if constexpr (LAYOUT == kDenseRowB) return info<CfgLarge, LAYOUT>();
       else return info<CfgWide, LAYOUT, FQ>();
+    case kCfgSquare:
+      if constexpr (LAYOUT == kDenseRowB) return info<CfgLarge, LAYOUT>();
+      else return info<CfgSquare, LAYOUT, FQ>();
     case kCfgDec64: return info<CfgDec64, LAYOUT, FQ>();
     case kCfgDec128: return info<CfgDec128, LAYOUT, FQ>();
-    case kCfgRows128:
-      if constexpr (FQ) return info<CfgLarge, LAYOUT, FQ>();   // the dense plan never picks it
+    case kCfgRows128:   // only the contiguous layout's plan picks it
+      if constexpr (FQ || LAYOUT == kDenseRowB) return info<CfgLarge, LAYOUT, FQ>();
       else return info<CfgRows128, LAYOUT>();
     default: return info<CfgLarge, LAYOUT, FQ>();
   }
@@ -798,18 +1015,21 @@ static int last_round_splits(int64_t tiles, int64_t grid, int kb_total) {
 }
 
 // Large-m tile choice: estimated time = rounds of the persistent grid x time per tile round.  A
-// 256x192 tile round takes ~1.22x a 256x128 round (1.5x the MFMA work, less operand traffic per
-// flop; measured on MI355X over nine shapes with M = 2048..16384), so it wins where it saves a
-// round, e.g. 4096x2112 (198 tiles, one round, vs 288) or 4096x7168 (3 rounds vs 3.5).
+// round of 256x192 tiles takes ~1.30x and a round of 256x256 tiles ~1.70x a round of 256x128 tiles
+// (1.5x and 2x the MFMA work; less operand traffic per flop; measured on MI355X over DeepSeek-V3
+// shapes with M = 4096, 8192 and 16384), so the larger tiles win where they save rounds, e.g.
+// 4096 x 4096 (256 tiles of 256x256: one round, against two of 256x128).
 static int choose_large(int64_t m, int64_t n, int64_t groups, int num_cus, int kb_total, bool split_tail) {
   auto rounds = [&](int bn, int bm) {
     const int64_t tiles = ((m + bm - 1) / bm) * ((n + bn - 1) / bn) * groups;
-    // both configurations run one workgroup per CU; a split last round counts 1/splits of a round
+    // every configuration runs one workgroup per CU; a split last round counts 1/splits of a round
     const int s = split_tail ? last_round_splits(tiles, num_cus, kb_total) : 1;
     return s > 1 ? (double)(tiles / num_cus) + 1.0 / s : (double)((tiles + num_cus - 1) / num_cus);
   };
   const double t_large = (double)rounds(CfgLarge::BN, CfgLarge::BM);
-  const double t_wide = 1.22 * (double)rounds(CfgWide::BN, CfgWide::BM);
+  const double t_wide = 1.30 * (double)rounds(CfgWide::BN, CfgWide::BM);
+  const double t_square = 1.70 * (double)rounds(CfgSquare::BN, CfgSquare::BM);
+  if (t_square < t_large && t_square < t_wide) return kCfgSquare;
   return t_wide < t_large ? kCfgWide : kCfgLarge;
 }
 

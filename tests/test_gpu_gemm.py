@@ -357,3 +357,63 @@ def test_cu_cap(cap):
         test_contiguous_small()
     finally:
         dg.dg_set_num_cus(full)
+
+
+# ---- the 256x192 and 256x256 tiles (two-slot pipelined main loop): K block counts 1, 2, odd,
+# partial; edges -------------------------------------------------------------------------------
+
+def _cap_for(prefix, layout, m, n, k, groups=1):
+    """The largest CU cap under which the planner gives this shape a configuration starting with
+    `prefix` (the cap changes how many rounds each tile size needs), or None."""
+    full = dg.dg_get_num_cus()
+    try:
+        for cap in range(full, 0, -1):
+            dg.dg_set_num_cus(cap)
+            if dg.dg_gemm_config_name(layout, m, n, k, groups).startswith(prefix):
+                return cap
+    finally:
+        dg.dg_set_num_cus(full)
+    return None
+
+
+_WIDE_SHAPES = [(300, 500, 16), (300, 500, 128), (300, 500, 256), (300, 500, 384), (300, 500, 400),
+                (520, 1000, 1280), (257, 193, 2064), (777, 2000, 3200)]
+_SQUARE_SHAPES = [(500, 500, 16), (500, 500, 128), (500, 500, 256), (500, 500, 384), (500, 500, 400),
+                  (512, 1000, 1280), (450, 300, 2064), (777, 2000, 3200)]
+
+
+@pytest.mark.parametrize("tile,m,n,k", [("256x192",) + s for s in _WIDE_SHAPES] +
+                                       [("256x256",) + s for s in _SQUARE_SHAPES])
+def test_wide_tile_k_blocks_and_edges(tile, m, n, k):
+    """The 256x192 and 256x256 tiles on shapes the planner gives them under a CU cap: one K block
+    (whole and partial), two, an odd count, a partial last group, and M / N edges inside a tile."""
+    cap = _cap_for(tile, 0, m, n, k)
+    assert cap is not None, (tile, m, n, k)
+    full = dg.dg_get_num_cus()
+    qa, sa, qb, sb = quantized_operands("wide", m, n, k)
+    try:
+        dg.dg_set_num_cus(cap)
+        name = dg.dg_gemm_config_name(0, m, n, k)
+        say("gemm wide tile", m, n, k, "cap", cap, name)
+        d1 = run_dense(qa, sa, qb, sb, ld_extra=4)
+        d2 = run_dense(qa, sa, qb, sb, ld_extra=4)
+    finally:
+        dg.dg_set_num_cus(full)
+    assert name.startswith(tile), name
+    assert np.array_equal(bf16_bits(d1), bf16_bits(d2))
+    check_gemm(d1, oracle.gemm.gemm_nt(qa, sa, qb, sb), f"wide {m}x{n}x{k} ({name})")
+
+
+@pytest.mark.parametrize("tile,m_max", [("256x192", 384), ("256x256", 512)])
+def test_wide_tile_masked(tile, m_max):
+    """The masked layout on the 256x192 and 256x256 tiles (groups partly or wholly empty)."""
+    g, n, k = 3, 500, 1024
+    cap = _cap_for(tile, 2, m_max, n, k, g)
+    assert cap is not None, tile
+    full = dg.dg_get_num_cus()
+    try:
+        dg.dg_set_num_cus(cap)
+        say("gemm wide tile masked", g, m_max, n, k, "cap", cap, dg.dg_gemm_config_name(2, m_max, n, k, g))
+        masked_case("masked_wide", g, m_max, n, k, [m_max, 200, 0])
+    finally:
+        dg.dg_set_num_cus(full)

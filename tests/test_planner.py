@@ -51,9 +51,9 @@ V3_PLANS = {
     (128, 2112, 7168): "64x64/4waves/split4", (128, 24576, 1536): "64x128/4waves/split1",
     (128, 32768, 512): "64x128/4waves/split1", (128, 7168, 16384): "64x128/4waves/split4",
     (128, 4096, 7168): "64x128/4waves/split4", (128, 7168, 2048): "64x64/4waves/split1",
-    (4096, 2112, 7168): "256x192/8waves/split1", (4096, 24576, 1536): "256x192/8waves/split1",
-    (4096, 32768, 512): "256x192/8waves/split1", (4096, 7168, 16384): "256x192/8waves/split1+tail2",
-    (4096, 4096, 7168): "256x192/8waves/split1+tail2", (4096, 7168, 2048): "256x192/8waves/split1",
+    (4096, 2112, 7168): "256x192/8waves/split1", (4096, 24576, 1536): "256x256/8waves/split1",
+    (4096, 32768, 512): "256x256/8waves/split1", (4096, 7168, 16384): "256x192/8waves/split1+tail2",
+    (4096, 4096, 7168): "256x256/8waves/split1", (4096, 7168, 2048): "256x256/8waves/split1",
 }
 
 
@@ -95,14 +95,16 @@ def test_plan_invariants_over_shapes():
             assert mt, (layout, m, n, k, g, name)
             bn, bm, waves, splits = (int(mt.group(i)) for i in range(1, 5))
             tail = mt.group(5)
-            assert (bn, bm, waves) in {(64, 64, 4), (64, 128, 4), (256, 128, 8), (256, 192, 8)}, name
+            assert (bn, bm, waves) in {(64, 64, 4), (64, 128, 4), (256, 128, 8), (256, 192, 8), (256, 256, 8)}, name
             assert 1 <= splits <= 16 and (tail is None or splits == 1)
             if tail is not None:
                 assert 2 <= int(tail) <= 16
             if layout == 1:   # the contiguous form never splits K (no workspace argument)
                 assert splits == 1 and tail is None, name
-            if layout == 3:   # per-row B scales leave no registers for the 256x192 tile
-                assert (bn, bm) != (256, 192), name
+            if layout == 3:   # per-row B scales run on the three-stage 256x128 tile only
+                assert (bn, bm) not in {(256, 192), (256, 256)}, name
+            if layout == 1:   # a contiguous tile spans one 128-row expert block
+                assert bm <= 128, name
             if layout == 0 and m <= 128:   # few rows: the 64-row weight tiles
                 assert bn == 64, (m, name)
             if layout in (0, 3) and m > 128:
