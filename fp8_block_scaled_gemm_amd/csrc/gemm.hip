@@ -395,8 +395,10 @@ __global__ __launch_bounds__(C::kThreads) void gemm_fp8_kernel(GemmParams p) {
     // DMA instruction u of this wave fills tile rows [8q, 8q+8) of a stage, q = wave + kWaves*u:
     // weights for u < kDmaB / kWaves, activations after.  Lane i writes slot i of that 1 KB (tile
     // row 8q + i/8, slot i%8), so it loads logical chunk (i%8) ^ f(row).  Each operand has one
-    // buffer resource based at the tile's first row and sized to the rows that exist: the hardware
-    // range check returns zeros for rows past the N or M edge (those outputs are never stored).
+    // buffer resource based at the tile's first row and sized to the rows that exist (for the
+    // masked layout: the group's valid rows, so its padding rows cost no memory traffic): the
+    // hardware range check returns zeros for rows past the N or M edge (those outputs are never
+    // stored).
     constexpr int kBandRows = 8 * C::kIssuers;
     constexpr int kBandsB = C::kDmaB / C::kIssuers;
     const int iw = wave - (C::kWaves - C::kIssuers);   // index among the issuing waves (< 0: not one)
@@ -412,7 +414,7 @@ __global__ __launch_bounds__(C::kThreads) void gemm_fp8_kernel(GemmParams p) {
     const __amdgpu_buffer_rsrc_t rs_b =
         make_rsrc(b_g + (int64_t)n0 * ld, p.n > n0 ? (int64_t)(p.n - n0 - 1) * ld + p.k : 0);
     const __amdgpu_buffer_rsrc_t rs_a =
-        make_rsrc(a_g + (int64_t)m0 * ld, p.m > m0 ? (int64_t)(p.m - m0 - 1) * ld + p.k : 0);
+        make_rsrc(a_g + (int64_t)m0 * ld, t.m_valid > m0 ? (int64_t)(t.m_valid - m0 - 1) * ld + p.k : 0);
     // activation scales: lanes [kSaLanesPerWave*wave, +kSaLanesPerWave) of the BM/4 16-byte chunks
     // of sa[kb][m0 .. m0+BM); chunks are clamped to the caller's ld_sa row (rows >= m are never stored)
     const int sa_lane = iw * C::kSaLanesPerWave + lane;
@@ -915,9 +917,11 @@ static LaunchInfo info() {
 }
 
 // Tile configurations: BN x BM workgroup tile, WN x WM wave tile, LDS stages.
-//  kCfgLarge   256x128, 8 waves of 64x64, 3 stages (~147 KB LDS): compute-bound shapes.
-//  kCfgRows128 256x128 for the contiguous layout (the expert changes every 128 rows, so no tile
-//              spans more): 8 waves of 64x64, two slots (~104 KB LDS), the pipelined main loop.
+//  kCfgLarge   256x128, 8 waves of 64x64, 3 stages (~147 KB LDS), the three-stage loop: the per-row
+//              B scales of the weight-gradient GEMM (no room for them in the pipelined loop).
+//  kCfgRows128 256x128, 8 waves of 64x64, two slots (~104 KB LDS), the pipelined main loop: the
+//              contiguous layout (the expert changes every 128 rows, so no tile spans more) and
+//              the 256x128 choice of the dense and masked forms.
 //  kCfgWide    256x192, 8 waves of 128x48, two slots (~120 KB LDS), the pipelined main loop: 1.5x
 //              the work per tile and ~1/6 less operand traffic per flop than kCfgLarge.
 //  kCfgSquare  256x256, 8 waves of 128x64, two slots (~136 KB LDS), the pipelined main loop: 2x the
@@ -950,9 +954,9 @@ static LaunchInfo cfg_info(int cfg) {
       else return info<CfgSquare, LAYOUT, FQ>();
     case kCfgDec64: return info<CfgDec64, LAYOUT, FQ>();
     case kCfgDec128: return info<CfgDec128, LAYOUT, FQ>();
-    case kCfgRows128:   // only the contiguous layout's plan picks it
-      if constexpr (FQ || LAYOUT == kDenseRowB) return info<CfgLarge, LAYOUT, FQ>();
-      else return info<CfgRows128, LAYOUT>();
+    case kCfgRows128:
+      if constexpr (LAYOUT == kDenseRowB) return info<CfgLarge, LAYOUT>();
+      else return info<CfgRows128, LAYOUT, FQ>();
     default: return info<CfgLarge, LAYOUT, FQ>();
   }
 }
@@ -1015,22 +1019,28 @@ static int last_round_splits(int64_t tiles, int64_t grid, int kb_total) {
 }
 
 // Large-m tile choice: estimated time = rounds of the persistent grid x time per tile round.  A
-// round of 256x192 tiles takes ~1.30x and a round of 256x256 tiles ~1.70x a round of 256x128 tiles
-// (1.5x and 2x the MFMA work; less operand traffic per flop; measured on MI355X over DeepSeek-V3
-// shapes with M = 4096, 8192 and 16384), so the larger tiles win where they save rounds, e.g.
-// 4096 x 4096 (256 tiles of 256x256: one round, against two of 256x128).
+// round of 256x192 tiles takes ~1.45x and a round of 256x256 tiles ~1.85x a round of 256x128
+// tiles (1.5x and 2x the MFMA work, less operand traffic per flop; measured on MI355X over
+// DeepSeek-V3 shapes with M = 2048 .. 16384, all three on the pipelined main loop).  A partial
+// last round with a fraction f of the CUs busy costs ~0.3 + 0.7 f of a full one (fewer workgroups
+// share the L2s and HBM), a split last round 1/splits + 0.1 (the hand-off).  The larger tiles win
+// where they save rounds, e.g. 4096 x 4096 (256 tiles of 256x256: one round, against two).
 static int choose_large(int64_t m, int64_t n, int64_t groups, int num_cus, int kb_total, bool split_tail) {
   auto rounds = [&](int bn, int bm) {
     const int64_t tiles = ((m + bm - 1) / bm) * ((n + bn - 1) / bn) * groups;
-    // every configuration runs one workgroup per CU; a split last round counts 1/splits of a round
+    // every configuration runs one workgroup per CU
     const int s = split_tail ? last_round_splits(tiles, num_cus, kb_total) : 1;
-    return s > 1 ? (double)(tiles / num_cus) + 1.0 / s : (double)((tiles + num_cus - 1) / num_cus);
+    const double full = (double)(tiles / num_cus);
+    const int64_t rest = tiles % num_cus;
+    if (rest == 0) return full;
+    if (s > 1) return full + 1.0 / s + 0.1;
+    return full + 0.3 + 0.7 * (double)rest / (double)num_cus;
   };
-  const double t_large = (double)rounds(CfgLarge::BN, CfgLarge::BM);
-  const double t_wide = 1.30 * (double)rounds(CfgWide::BN, CfgWide::BM);
-  const double t_square = 1.70 * (double)rounds(CfgSquare::BN, CfgSquare::BM);
+  const double t_large = (double)rounds(CfgRows128::BN, CfgRows128::BM);
+  const double t_wide = 1.45 * (double)rounds(CfgWide::BN, CfgWide::BM);
+  const double t_square = 1.85 * (double)rounds(CfgSquare::BN, CfgSquare::BM);
   if (t_square < t_large && t_square < t_wide) return kCfgSquare;
-  return t_wide < t_large ? kCfgWide : kCfgLarge;
+  return t_wide < t_large ? kCfgWide : kCfgRows128;
 }
 
 // Few-row plan (m <= 128 rows per group): the K split from a model of the streaming regime, fitted to
@@ -1099,6 +1109,8 @@ static Plan make_plan(int layout, int64_t m, int64_t n, int64_t k, int64_t group
   pl.cfg = layout == kContiguous ? kCfgRows128
            : layout == kDenseRowB ? kCfgLarge
                                   : choose_large(m, n, groups, num_cus, kb_total, allow_split && layout == kDense);
+  // (the 256x128 tile of the dense and masked forms is the pipelined one, kCfgRows128; kCfgLarge,
+  // the three-stage loop, serves the per-row B scales)
   const LaunchInfo li = cfg_info<kDense>(pl.cfg);
   pl.splits = 1;
   pl.tail_start = 0;

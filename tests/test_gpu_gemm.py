@@ -55,7 +55,7 @@ def test_ragged_shapes(m, n, k):
     check_gemm(run_dense(qa, sa, qb, sb, ld_extra=4), ref, f"ragged {m}x{n}x{k}")
 
 
-@pytest.mark.parametrize("m,n,k", [(4608, 4096, 6144), (4096, 7168, 6144)])
+@pytest.mark.parametrize("m,n,k", [(4608, 4096, 6144), (4096, 6144, 6144), (4096, 5120, 6144)])
 def test_split_last_round(m, n, k):
     """More tiles than the persistent grid holds, with a partial last round and a long K: the whole
     tiles of the full rounds run unsplit and the last round's tiles are split in K (split1+tailN).
@@ -63,8 +63,8 @@ def test_split_last_round(m, n, k):
     (no-workspace) plan."""
     name = dg.dg_gemm_config_name(0, m, n, k)
     say("gemm split last round", m, n, k, name)
-    if dg.dg_get_num_cus() == 256:   # 256x192 tiles: 22 x 28 = 616 (tail 104), 24 x 16 = 384 (tail 128)
-        assert "+tail" in name, name
+    if dg.dg_get_num_cus() == 256:   # 256x192: 24 x 16 = 384 tiles (tail 128); 256x256: 16 x 24 = 384
+        assert "+tail" in name, name  # (tail 128); 256x128: 32 x 20 = 640 (tail 128)
     qa, sa, qb, sb = quantized_operands("tail", m, n, k)
     ref = oracle.gemm.gemm_nt(qa, sa, qb, sb)
     d1, d2 = run_dense(qa, sa, qb, sb), run_dense(qa, sa, qb, sb)
@@ -379,7 +379,7 @@ def _cap_for(prefix, layout, m, n, k, groups=1):
 _WIDE_SHAPES = [(300, 500, 16), (300, 500, 128), (300, 500, 256), (300, 500, 384), (300, 500, 400),
                 (520, 1000, 1280), (257, 193, 2064), (777, 2000, 3200)]
 _SQUARE_SHAPES = [(500, 500, 16), (500, 500, 128), (500, 500, 256), (500, 500, 384), (500, 500, 400),
-                  (512, 1000, 1280), (450, 300, 2064), (777, 2000, 3200)]
+                  (512, 1000, 1280), (450, 300, 2064), (1000, 2000, 3200)]
 
 
 @pytest.mark.parametrize("tile,m,n,k", [("256x192",) + s for s in _WIDE_SHAPES] +

@@ -52,7 +52,7 @@ V3_PLANS = {
     (128, 32768, 512): "64x128/4waves/split1", (128, 7168, 16384): "64x128/4waves/split4",
     (128, 4096, 7168): "64x128/4waves/split4", (128, 7168, 2048): "64x64/4waves/split1",
     (4096, 2112, 7168): "256x192/8waves/split1", (4096, 24576, 1536): "256x256/8waves/split1",
-    (4096, 32768, 512): "256x256/8waves/split1", (4096, 7168, 16384): "256x192/8waves/split1+tail2",
+    (4096, 32768, 512): "256x256/8waves/split1", (4096, 7168, 16384): "256x256/8waves/split1",
     (4096, 4096, 7168): "256x256/8waves/split1", (4096, 7168, 2048): "256x256/8waves/split1",
 }
 
@@ -74,10 +74,11 @@ def test_v3_dense_plans_on_256_cus():
 def test_split_last_round_plans():
     """Shapes with a partial last round of the persistent grid and a long K split only that round
     (the GPU tests assert the same names at 256 CUs)."""
-    got = plans([[0, 4608, 4096, 6144, 1], [0, 4096, 7168, 6144, 1], [3, 2048, 5120, 6144, 1],
-                 [0, 4096, 7168, 1024, 1]])
+    got = plans([[0, 4608, 4096, 6144, 1], [0, 4096, 6144, 6144, 1], [0, 4096, 5120, 6144, 1],
+                 [3, 2048, 5120, 6144, 1], [0, 4096, 7168, 1024, 1]])
     assert got[(0, 4608, 4096, 6144, 1)][0] == "256x192/8waves/split1+tail2"
-    assert got[(0, 4096, 7168, 6144, 1)][0] == "256x192/8waves/split1+tail2"
+    assert got[(0, 4096, 6144, 6144, 1)][0] == "256x256/8waves/split1+tail2"
+    assert got[(0, 4096, 5120, 6144, 1)][0] == "256x128/8waves/split1+tail2"
     assert got[(3, 2048, 5120, 6144, 1)][0] == "256x128/8waves/split1+tail2"
     assert "+tail" not in got[(0, 4096, 7168, 1024, 1)][0]   # pieces would be < 24 K blocks
 
