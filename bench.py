@@ -109,6 +109,7 @@ class Op:
         self.flops, self.nbytes, self.config = float(flops), float(nbytes), config
         self.weights, self.make = weights, make
         self.copies = None
+        self.rot = 1      # launches per timed event pair (weight copies)
         self.times = []   # ms per launch, one entry per timed step
 
 
@@ -632,10 +633,12 @@ def rooflines(workload, ops):
             by_k.setdefault(kernel_of(op.config), []).append(op)
     out = {}
     for kern, kops in by_k.items():
-        t = sum(sum(o.times) for o in kops) * 1e-3
-        launches = sum(len(o.times) for o in kops)
-        f = sum(o.flops * len(o.times) for o in kops)
-        b = sum(o.nbytes * len(o.times) for o in kops)
+        # every timed launch counts once (a GEMM timed over R weight copies is R launches), so the
+        # average launch duration is the one a kernel trace of the same run reports
+        t = sum(sum(o.times) * o.rot for o in kops) * 1e-3
+        launches = sum(len(o.times) * o.rot for o in kops)
+        f = sum(o.flops * len(o.times) * o.rot for o in kops)
+        b = sum(o.nbytes * len(o.times) * o.rot for o in kops)
         mfma = f / (PEAK_FP8_TFLOPS * 1e12) >= b / (PEAK_HBM_GBS * 1e9)
         if mfma:
             achieved, peak, unit = f / t / 1e12, PEAK_FP8_TFLOPS, "TFLOP/s"
@@ -647,7 +650,7 @@ def rooflines(workload, ops):
                      "traffic": traffic["bytes_per_launch"] if traffic else None, "traffic_detail": traffic,
                      "kernel": kern, "launches": launches, "avg_launch_us": round(t / launches * 1e6, 2),
                      "algorithmic_bytes_per_launch": round(b / launches), "flops_per_launch": round(f / launches),
-                     "device_us_per_step": round(t / max(1, len(kops[0].times)) * 1e6, 1),
+                     "device_us_per_step": round(sum(sum(o.times) for o in kops) * 1e-3 / max(1, len(kops[0].times)) * 1e6, 1),
                      "shapes": sorted({o.label for o in kops})}
     return out
 
@@ -704,6 +707,7 @@ def run_workload(name, args, torch, dg, dev, stream, flush_buf):
             wbytes = op.weights.numel() * op.weights.element_size()
             r = max(1, min(MAX_ROT, -(-ROT_BYTES // max(wbytes, 1))))
             op.copies = [op.weights] + [op.weights.clone() for _ in range(r - 1)]
+            op.rot = r
     torch.cuda.synchronize()
     cal0, cal1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     with torch.cuda.stream(stream):
@@ -743,13 +747,12 @@ def run_workload(name, args, torch, dg, dev, stream, flush_buf):
             continue
         t = float(np.median(op.times)) * 1e-3
         tf, gb = op.flops / t / 1e12, op.nbytes / t / 1e9
-        rot = max(1, min(MAX_ROT, -(-ROT_BYTES // max(op.weights.numel(), 1)))) if op.weights is not None else 1
         shapes.append({"shape": op.label, "config": op.config, "us": round(t * 1e6, 2),
                        "tflops": round(tf, 1), "gbps": round(gb, 1),
                        "mfma_frac": round(tf / PEAK_FP8_TFLOPS, 4), "hbm_frac": round(gb / PEAK_HBM_GBS, 4),
                        "roofline_frac": round(max(op.flops / (PEAK_FP8_TFLOPS * 1e12),
                                                   op.nbytes / (PEAK_HBM_GBS * 1e9)) / t, 4),
-                       "rotations": 1 if args.no_rotate else rot})
+                       "rotations": op.rot})
     kernels = rooflines(name, ops)
     dominant = max(kernels.values(), key=lambda r: r["avg_launch_us"] * r["launches"])
     quant = {}

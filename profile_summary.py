@@ -109,13 +109,15 @@ def source_digest():
 def cmd_traffic(args):
     with open(args.bench_json) as fh:
         bench = json.loads(fh.read().strip().splitlines()[-1])
-    # algorithmic bytes per launch per tile configuration, from bench.py's per-shape list
+    # algorithmic bytes per launch per tile configuration, from bench.py's per-shape list, each
+    # shape weighted by its launches per timed step (its weight copies), as the counter runs
+    # dispatch it
     alg = defaultdict(list)
     for sh in bench["shapes"]:
         cfg = "gemm_fp8_kernel " + sh["config"].split("/split")[0]
         if sh["config"].endswith("+act-quant"):
             cfg += " +act-quant"
-        alg[cfg].append(sh["gbps"] * sh["us"] * 1e3)   # bytes = GB/s * us * 1e3
+        alg[cfg] += [sh["gbps"] * sh["us"] * 1e3] * int(sh.get("rotations", 1))   # bytes = GB/s * us * 1e3
     ff, fk, fv = copy_factor(args.copy_fetch, "FETCH_SIZE")
     wf, wk, wv = copy_factor(args.copy_write, "WRITE_SIZE")
     fetch = counter_per_dispatch(args.fetch, "FETCH_SIZE")
