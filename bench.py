@@ -4,6 +4,7 @@
                      large_dense|zipf|train_v3|train_moe|overlap] [--no-flush] [--no-rotate]
                      [--no-cpu-baseline] [--cpu-seconds S] [--eager]
     python bench.py --copy-calibration      # counter calibration: one plain 1 GiB device copy
+    python bench.py --plan-sweep [--out F]  # every few-row plan of the M = 64 / 128 shapes, timed
 
 By default every configuration of the benchmark set runs (small, dense_v3, contiguous,
 masked, large_dense, zipf); dense_v3 - the DeepSeek-V3 dense shapes at M in {64, 128, 4096} -
@@ -82,6 +83,9 @@ def parse():
                     help="device spin before each per-kernel timing pass (covers the host's enqueue time)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy (calibrates the FETCH_SIZE / WRITE_SIZE counters)")
+    ap.add_argument("--plan-sweep", action="store_true",
+                    help="only time every few-row plan (tile x K split) of the M = 64 / 128 DeepSeek-V3 shapes")
+    ap.add_argument("--out", default="", help="--plan-sweep: also write the markdown table here")
     return ap.parse_args()
 
 
@@ -611,6 +615,77 @@ def copy_calibration(torch, dev, nbytes=1 << 30, reps=5):
     print(json.dumps({"copy_calibration_bytes": nbytes, "launches": reps}), flush=True)
 
 
+def plan_sweep(args, torch, dg, dev):
+    """Every few-row plan the planner weighs (64x64 and 64x128 tiles x K splits 1..16, forced with
+    DG_PLAN) on the twelve M = 64 / 128 DeepSeek-V3 shapes, timed like bench.py's per-launch pass
+    (R launches over rotated weight copies after a 512 MB write, median of 5), next to the plan the
+    planner picks.  Writes a markdown table (the evidence behind the few-row planner's model)."""
+    from fp8_block_scaled_gemm_amd import inputs
+    gen = Gen(torch, dev, 99)
+    flush = torch.empty(FLUSH_BYTES, dtype=torch.uint8, device=dev)
+    ws = torch.zeros(256 << 20, dtype=torch.uint8, device=dev)
+    lines = ["| shape | planner's plan | us | GB/s | best plan | us | GB/s | planner / best |",
+             "|---|---|---|---|---|---|---|---|"]
+    detail = []
+    old_plan = os.environ.pop("DG_PLAN", None)
+    for m in (64, 128):
+        for (n, k) in inputs.DENSE_V3_NK:
+            qa, sa = dg.dg_quantize_per_token_group(gen.activations(m, k))
+            qb, sb = dg.dg_quantize_per_block(gen.normal((n, k), 0.02))
+            r = max(1, min(MAX_ROT, -(-ROT_BYTES // (n * k))))
+            copies = [qb] + [qb.clone() for _ in range(r - 1)]
+            d = torch.empty((m, n), dtype=torch.bfloat16, device=dev)
+            wbytes = dense_gemm_bytes(m, n, k)
+
+            def timed():
+                for w in copies:
+                    dg.dg_gemm_fp8_nt(qa, sa, w, sb, d=d, workspace=ws)
+                torch.cuda.synchronize()
+                ts = []
+                for rep in range(5):
+                    flush.fill_(rep)
+                    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                    e0.record()
+                    for w in copies:
+                        dg.dg_gemm_fp8_nt(qa, sa, w, sb, d=d, workspace=ws)
+                    e1.record()
+                    torch.cuda.synchronize()
+                    ts.append(e0.elapsed_time(e1) * 1e3 / r)
+                return float(np.median(ts))
+
+            default = dg.dg_gemm_config_name(0, m, n, k)
+            t_default = timed()
+            results = {default: t_default}
+            for tile in ("64x64", "64x128"):
+                for sp in (1, 2, 3, 4, 6, 8, 12, 16):
+                    os.environ["DG_PLAN"] = f"tile={tile},splits={sp}"
+                    name = dg.dg_gemm_config_name(0, m, n, k)
+                    if name not in results:
+                        results[name] = timed()
+            os.environ.pop("DG_PLAN", None)
+            best = min(results, key=results.get)
+            shape = f"{m}x{n}x{k}"
+            print(f"[bench] plan sweep {shape}: planner {default} {t_default:.1f} us, best {best} "
+                  f"{results[best]:.1f} us", file=sys.stderr, flush=True)
+            lines.append(f"| {shape} | {default} | {t_default:.1f} | {wbytes / t_default / 1e3:.0f} | {best} | "
+                         f"{results[best]:.1f} | {wbytes / results[best] / 1e3:.0f} | {t_default / results[best]:.2f} |")
+            detail.append(f"| {shape} | " + ", ".join(f"{nm.split('/')[0]} s{nm.split('split')[1]}: {t:.1f}"
+                                                   for nm, t in sorted(results.items())) + " |")
+            del copies
+    if old_plan is not None:
+        os.environ["DG_PLAN"] = old_plan
+    out = ["# Few-row plans: every tile x K split the planner weighs, against its choice", "",
+           "Command:", "", "```", "python3 bench.py --plan-sweep --out profiles/decode_plan_sweep.md", "```", "",
+           "Per launch, R launches over rotated weight copies (> 768 MB) after an untimed 512 MB write, "
+           "median of 5; GB/s = algorithmic bytes (A, B, their scales, bf16 D) / time.  Plans forced with "
+           "DG_PLAN.", ""] + lines + ["", "All plans (us):", "", "| shape | tile, split: us |", "|---|---|"] + detail
+    text = "\n".join(out) + "\n"
+    if args.out:
+        with open(args.out, "w") as fh:
+            fh.write(text)
+    print(text)
+
+
 DEFAULT_SET = ["small", "dense_v3", "contiguous", "masked", "large_dense", "zipf"]
 HEADLINE = "dense_v3"
 ROT_BYTES = 768 << 20     # weight copies a GEMM's timed launches rotate over: > 3x the 256 MB MALL
@@ -792,6 +867,10 @@ def main():
     dev = torch.device("cuda", 0)
     if args.copy_calibration:
         copy_calibration(torch, dev)
+        return
+    if args.plan_sweep:
+        dg.lib()
+        plan_sweep(args, torch, dg, dev)
         return
     dg.lib()
     if args.num_cus > 0:

@@ -46,6 +46,7 @@
 //    faster one.
 #include <cstdio>
 #include <cstdlib>
+#include <cstring>
 #include <mutex>
 #include <type_traits>
 
@@ -1101,8 +1102,56 @@ static Plan make_decode_plan(int64_t m, int64_t n, int64_t k, int64_t groups, in
   return pl;
 }
 
+static Plan make_plan_auto(int layout, int64_t m, int64_t n, int64_t k, int64_t groups, int num_cus,
+                           bool allow_split);
+
+// DG_PLAN: a measurement override of the planner's choice, "tile=BNxBM" and / or "splits=S"
+// (comma-separated; e.g. "tile=64x128,splits=4").  The tile must be one the planner could pick for
+// the form and size (64x64 or 64x128 for m <= 128; 256x128, 256x192 or 256x256 above, 256x128 for
+// the contiguous form); anything else is ignored.  Splits apply where the call may split K, as a
+// split of every tile.  Read at every call, like DG_DEBUG; the workspace queries see the same plan.
+static void apply_plan_override(Plan& pl, int layout, int64_t m, int kb_total, bool allow_split) {
+  const char* e = std::getenv("DG_PLAN");
+  if (e == nullptr || e[0] == '\0') return;
+  int bn = 0, bm = 0, want = 0;
+  for (const char* q = e; *q;) {
+    if (std::sscanf(q, "tile=%dx%d", &bn, &bm) == 2 || std::sscanf(q, "splits=%d", &want) == 1) {}
+    const char* c = std::strchr(q, ',');
+    if (c == nullptr) break;
+    q = c + 1;
+  }
+  if (bn > 0) {
+    static const int kDecCfgs[] = {kCfgDec64, kCfgDec128};
+    static const int kLargeCfgs[] = {kCfgRows128, kCfgWide, kCfgSquare};
+    const bool few = layout != kContiguous && m <= 128;
+    const int* list = few ? kDecCfgs : kLargeCfgs;
+    const int count = few ? 2 : (layout == kContiguous || layout == kDenseRowB ? 1 : 3);
+    for (int i = 0; i < count; ++i) {
+      const LaunchInfo li = cfg_info<kDense>(list[i]);
+      if (li.bn == bn && li.bm == bm) pl.cfg = layout == kDenseRowB && !few ? kCfgLarge : list[i];
+    }
+  }
+  if (want > 0 && allow_split && layout != kContiguous) {
+    if (want > kMaxSplits) want = kMaxSplits;
+    pl.kb_per_split = (kb_total + want - 1) / want;
+    pl.splits = (kb_total + pl.kb_per_split - 1) / pl.kb_per_split;
+    pl.tail_start = 0;
+  }
+}
+
 // Pick the tile config and the K split.  `groups` multiplies the tile count (masked layout).
 static Plan make_plan(int layout, int64_t m, int64_t n, int64_t k, int64_t groups, int num_cus, bool allow_split) {
+  Plan pl = make_plan_auto(layout, m, n, k, groups, num_cus, allow_split);
+  if (const char* e = std::getenv("DG_PLAN"); e != nullptr && e[0] != '\0') {
+    apply_plan_override(pl, layout, m, (int)((k + kGroup - 1) / kGroup), allow_split);
+    finish_plan(pl, m, n, k, groups);
+  }
+  return pl;
+}
+
+// The planner's own choice.
+static Plan make_plan_auto(int layout, int64_t m, int64_t n, int64_t k, int64_t groups, int num_cus,
+                           bool allow_split) {
   if (layout != kContiguous && m <= 128) return make_decode_plan(m, n, k, groups, num_cus, allow_split);
   Plan pl{};
   const int kb_total = (int)((k + kGroup - 1) / kGroup);

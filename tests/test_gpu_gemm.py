@@ -417,3 +417,25 @@ def test_wide_tile_masked(tile, m_max):
         masked_case("masked_wide", g, m_max, n, k, [m_max, 200, 0])
     finally:
         dg.dg_set_num_cus(full)
+
+
+def test_plan_override_results():
+    """Plans forced with DG_PLAN (the planner's alternatives) give results within the GEMM
+    tolerance of the oracle: a few-row tile and split the planner did not pick, and a large tile."""
+    import os
+    cases = [((64, 2112, 1024), "tile=64x128,splits=3"), ((300, 1000, 1024), "tile=256x256,splits=2")]
+    for (m, n, k), plan in cases:
+        qa, sa, qb, sb = quantized_operands("override", m, n, k)
+        old = os.environ.get("DG_PLAN")
+        os.environ["DG_PLAN"] = plan
+        try:
+            name = dg.dg_gemm_config_name(0, m, n, k)
+            say("gemm forced plan", m, n, k, plan, name)
+            d = run_dense(qa, sa, qb, sb)
+        finally:
+            if old is None:
+                os.environ.pop("DG_PLAN", None)
+            else:
+                os.environ["DG_PLAN"] = old
+        assert name.split("/")[0] == plan.split(",")[0][len("tile="):], name
+        check_gemm(d, oracle.gemm.gemm_nt(qa, sa, qb, sb), f"forced {plan} {m}x{n}x{k}")

@@ -32,11 +32,15 @@ print(json.dumps(out))
 """
 
 
-def plans(cases, cus=256):
+def plans(cases, cus=256, plan_override=None):
     if not os.path.exists(LIB):
         pytest.fail("libdg.so is not built: run `python -m fp8_block_scaled_gemm_amd._build`")
+    env = dict(os.environ)
+    env.pop("DG_PLAN", None)
+    if plan_override is not None:
+        env["DG_PLAN"] = plan_override
     r = subprocess.run([sys.executable, "-c", _QUERY.format(root=ROOT, cus=cus), json.dumps(cases)],
-                       capture_output=True, text=True, timeout=120)
+                       capture_output=True, text=True, timeout=120, env=env)
     assert r.returncode == 0, r.stderr[-2000:]
     return {tuple(row[:5]): tuple(row[5:]) for row in json.loads(r.stdout.strip().splitlines()[-1])}
 
@@ -114,3 +118,33 @@ def test_plan_invariants_over_shapes():
                 assert ws > 0, (layout, m, n, k, g, name)   # a split plan has its workspace size
             kb = -(-k // 128)
             assert splits <= kb and int(tail or 1) <= kb
+
+
+def test_plan_override():
+    """DG_PLAN replaces the planner's tile and K split where they are valid for the form and size,
+    the workspace query follows the overridden plan, and anything else leaves the plan alone."""
+    cases = [[0, 64, 2112, 7168, 1], [0, 4096, 2112, 7168, 1], [1, 4096, 2112, 7168, 4], [3, 4096, 2112, 7168, 1],
+             [2, 128, 4096, 7168, 8]]
+    base = plans(cases)
+    got = plans(cases, plan_override="tile=64x128,splits=3")
+    assert got[(0, 64, 2112, 7168, 1)][0] == "64x128/4waves/split3"
+    # 56 K blocks in 3 splits of 19: a split tile needs 64 x 128 x 4 bytes per split
+    assert got[(0, 64, 2112, 7168, 1)][1] == 64 * 1024 + 33 * 3 * 64 * 128 * 4
+    assert got[(0, 4096, 2112, 7168, 1)][0] == base[(0, 4096, 2112, 7168, 1)][0].split("/split")[0] + "/split3"
+    assert got[(1, 4096, 2112, 7168, 4)][0] == base[(1, 4096, 2112, 7168, 4)][0]   # contiguous: no split
+    assert got[(2, 128, 4096, 7168, 8)][0] == "64x128/4waves/split3"
+    got = plans(cases, plan_override="tile=256x256")
+    assert got[(0, 4096, 2112, 7168, 1)][0].startswith("256x256/8waves/")
+    assert got[(1, 4096, 2112, 7168, 4)][0].startswith("256x128/")   # contiguous: 256x128 only
+    assert got[(3, 4096, 2112, 7168, 1)][0].startswith("256x128/")   # row-scaled: 256x128 only
+    assert got[(0, 64, 2112, 7168, 1)] == base[(0, 64, 2112, 7168, 1)]   # not a few-row tile
+    for junk in ("tile=100x7", "splits=0", "nonsense", "tile=64x64,splits=99"):
+        got = plans(cases, plan_override=junk)
+        for key, val in got.items():
+            if junk.endswith("99") and key[0] != 1 and key[1] <= 128:
+                kb = -(-key[3] // 128)   # capped at 16 splits, none of them empty
+                assert val[0] == f"64x64/4waves/split{-(-kb // -(-kb // 16))}", (junk, key, val)
+            elif junk.endswith("99"):
+                pass
+            else:
+                assert val == base[key], (junk, key, val)
