@@ -180,7 +180,8 @@ __device__ __forceinline__ void wait_groups(int younger) {
 }
 
 struct TileCoord {
-  int g, mb, nbt, split, m_valid;
+  int g, mb, nbt, split;
+  int m_lo, m_valid;   // the tile's output rows are those in [m_lo, m_valid)
 };
 
 // ---- activation quantization inside the GEMM launch (dense layout) ---------------------------
@@ -342,9 +343,17 @@ __global__ __launch_bounds__(C::kThreads) void gemm_fp8_kernel(GemmParams p) {
   int wg = blockIdx.x;
   if ((grid & 7) == 0) wg = (blockIdx.x & 7) * (grid >> 3) + (blockIdx.x >> 3);
 
-  for (int item = wg; item < total_items; item += grid) {
+  // The contiguous layout on 256-row tiles: a tile whose two 128-row halves belong to different
+  // experts runs twice (pass 0 with the first half's expert, pass 1 with the second's), each pass
+  // storing only its own half.  Every other tile runs once.
+  constexpr bool kTwoPass = LAYOUT == kContiguous && C::BM > kGroup;
+  int step = grid, next_pass = 0;
+  for (int item = wg, pass = 0; item < total_items; item += step, pass = next_pass) {
+    step = grid;
+    next_pass = 0;
     // ---- decode the item ------------------------------------------------------
     TileCoord t;
+    t.m_lo = 0;
     // whole tile (item < tail_start) or split `t.split` of split tile `sidx`
     const bool split_item = item >= p.tail_start;
     const int sidx = (item - p.tail_start) / p.splits;
@@ -380,8 +389,22 @@ __global__ __launch_bounds__(C::kThreads) void gemm_fp8_kernel(GemmParams p) {
     int expert = t.g;
     if constexpr (LAYOUT == kContiguous) {
       expert = p.m_indices[m0];
-      if (p.debug) check_contiguous_block<NT, C::BM>(p.m_indices, p.m, p.num_groups, m0);
-      if (expert < 0 || expert >= p.num_groups) continue;   // uniform: skip unmapped block
+      if (p.debug && pass == 0) check_contiguous_block<NT, C::BM>(p.m_indices, p.m, p.num_groups, m0);
+      if constexpr (kTwoPass) {
+        static_assert(C::BM == 2 * kGroup, "a contiguous tile spans one or two 128-row expert blocks");
+        const int e1 = m0 + kGroup < p.m ? p.m_indices[m0 + kGroup] : expert;
+        if (e1 != expert) {   // uniform: the halves name different experts (or one is unmapped)
+          if (pass == 0) {
+            step = 0;          // the same item again, as pass 1
+            next_pass = 1;
+            t.m_valid = m0 + kGroup;
+          } else {
+            expert = e1;
+            t.m_lo = m0 + kGroup;
+          }
+        }
+      }
+      if (expert < 0 || expert >= p.num_groups) continue;   // uniform: skip an unmapped block or half
     }
     const int kb_begin = split_item ? t.split * p.kb_per_split : 0;
     int kb_end = split_item ? kb_begin + p.kb_per_split : p.kb_total;
@@ -864,7 +887,7 @@ __global__ __launch_bounds__(C::kThreads) void gemm_fp8_kernel(GemmParams p) {
           const u32x4 val = *reinterpret_cast<const u32x4*>(strip + row * kPitch + cc * 16);
           const int mrow = m0 + wm0 + 16 * j + row;
           const int ncol = n0 + wn0 + 8 * cc;
-          if (mrow < t.m_valid && ncol < p.n)
+          if ((!kTwoPass || mrow >= t.m_lo) && mrow < t.m_valid && ncol < p.n)
             *reinterpret_cast<u32x4*>(d_g + (int64_t)mrow * p.n + ncol) = val;
         }
       }
@@ -874,7 +897,7 @@ __global__ __launch_bounds__(C::kThreads) void gemm_fp8_kernel(GemmParams p) {
 #pragma unroll
     for (int j = 0; j < C::kFragM; ++j) {
       const int mrow = m0 + wm0 + 16 * j + l16;
-      if (mrow >= t.m_valid) continue;
+      if ((kTwoPass && mrow < t.m_lo) || mrow >= t.m_valid) continue;
       uint16_t* drow = d_g + (int64_t)mrow * p.n;
 #pragma unroll
       for (int i = 0; i < C::kFragN; ++i) {
@@ -921,14 +944,16 @@ static LaunchInfo info() {
 //  kCfgLarge   256x128, 8 waves of 64x64, 3 stages (~147 KB LDS), the three-stage loop: the per-row
 //              B scales of the weight-gradient GEMM (no room for them in the pipelined loop).
 //  kCfgRows128 256x128, 8 waves of 64x64, two slots (~104 KB LDS), the pipelined main loop: the
-//              contiguous layout (the expert changes every 128 rows, so no tile spans more) and
-//              the 256x128 choice of the dense and masked forms.
+//              256x128 choice of the dense, masked and contiguous forms (a contiguous tile of it
+//              lies in one 128-row expert block).
 //  kCfgWide    256x192, 8 waves of 128x48, two slots (~120 KB LDS), the pipelined main loop: 1.5x
 //              the work per tile and ~1/6 less operand traffic per flop than kCfgLarge.
 //  kCfgSquare  256x256, 8 waves of 128x64, two slots (~136 KB LDS), the pipelined main loop: 2x the
 //              work per tile, 1/4 less operand traffic per flop than kCfgLarge and 1/6 fewer LDS
 //              reads per MFMA than kCfgWide.  The planner picks whichever of the three needs the
 //              least time in rounds of the persistent grid (wave quantisation decides most shapes).
+//              In the contiguous form a tile spans two 128-row expert blocks and runs once per
+//              expert when they differ.
 //  kCfgDec*    m <= 128 rows: 64 weight rows x 64 or 128 activation rows, 4 waves, two
 //              workgroups per CU: HBM-bound shapes (for 65..128 rows the planner's model picks
 //              one 128-row or two 64-row activation tiles).  (Measured against 128-row weight
@@ -949,6 +974,8 @@ static LaunchInfo cfg_info(int cfg) {
     // have no room for them, so kDenseRowB runs its large shapes on 256x128
     case kCfgWide:
       if constexpr (LAYOUT == kDenseRowB) return info<CfgLarge, LAYOUT>();
+      // 192-row tiles would cut 128-row expert blocks: the contiguous form has no such tile
+      else if constexpr (LAYOUT == kContiguous) return info<CfgRows128, LAYOUT>();
       else return info<CfgWide, LAYOUT, FQ>();
     case kCfgSquare:
       if constexpr (LAYOUT == kDenseRowB) return info<CfgLarge, LAYOUT>();
@@ -1026,22 +1053,41 @@ static int last_round_splits(int64_t tiles, int64_t grid, int kb_total) {
 // last round with a fraction f of the CUs busy costs ~0.3 + 0.7 f of a full one (fewer workgroups
 // share the L2s and HBM), a split last round 1/splits + 0.1 (the hand-off).  The larger tiles win
 // where they save rounds, e.g. 4096 x 4096 (256 tiles of 256x256: one round, against two).
+static double tile_rounds(int64_t tiles, int num_cus, int splits) {
+  // every large-tile configuration runs one workgroup per CU
+  const double full = (double)(tiles / num_cus);
+  const int64_t rest = tiles % num_cus;
+  if (rest == 0) return full;
+  if (splits > 1) return full + 1.0 / splits + 0.1;
+  return full + 0.3 + 0.7 * (double)rest / (double)num_cus;
+}
+
 static int choose_large(int64_t m, int64_t n, int64_t groups, int num_cus, int kb_total, bool split_tail) {
   auto rounds = [&](int bn, int bm) {
     const int64_t tiles = ((m + bm - 1) / bm) * ((n + bn - 1) / bn) * groups;
-    // every configuration runs one workgroup per CU
-    const int s = split_tail ? last_round_splits(tiles, num_cus, kb_total) : 1;
-    const double full = (double)(tiles / num_cus);
-    const int64_t rest = tiles % num_cus;
-    if (rest == 0) return full;
-    if (s > 1) return full + 1.0 / s + 0.1;
-    return full + 0.3 + 0.7 * (double)rest / (double)num_cus;
+    return tile_rounds(tiles, num_cus, split_tail ? last_round_splits(tiles, num_cus, kb_total) : 1);
   };
   const double t_large = (double)rounds(CfgRows128::BN, CfgRows128::BM);
   const double t_wide = 1.45 * (double)rounds(CfgWide::BN, CfgWide::BM);
   const double t_square = 1.85 * (double)rounds(CfgSquare::BN, CfgSquare::BM);
   if (t_square < t_large && t_square < t_wide) return kCfgSquare;
   return t_wide < t_large ? kCfgWide : kCfgRows128;
+}
+
+// Contiguous-layout tile choice between 256x128 (one 128-row expert block per tile) and 256x256
+// (two blocks; a tile whose blocks name different experts runs once per block), by the same
+// rounds estimate.  The host does not see m_indices: the 256x256 estimate counts one extra tile
+// per expert boundary in each n-tile column (experts - 1 of them, at most one per 256-row block),
+// as if every boundary fell inside a tile.  Large experts (a few thousand rows each) take
+// 256x256; many small ones (e.g. 64 experts of a few hundred rows) keep 256x128.
+static int choose_contiguous(int64_t m, int64_t n, int64_t experts, int num_cus) {
+  const int64_t tiles_n = (n + CfgSquare::BN - 1) / CfgSquare::BN;
+  const int64_t blocks = (m + CfgSquare::BM - 1) / CfgSquare::BM;
+  int64_t boundaries = experts - 1 < blocks ? experts - 1 : blocks;
+  if (boundaries < 0) boundaries = 0;
+  const double t_rows = tile_rounds(((m + CfgRows128::BM - 1) / CfgRows128::BM) * tiles_n, num_cus, 1);
+  const double t_square = 1.85 * tile_rounds((blocks + boundaries) * tiles_n, num_cus, 1);
+  return t_square < t_rows ? kCfgSquare : kCfgRows128;
 }
 
 // Few-row plan (m <= 128 rows per group): the K split from a model of the streaming regime, fitted to
@@ -1107,8 +1153,8 @@ static Plan make_plan_auto(int layout, int64_t m, int64_t n, int64_t k, int64_t 
 
 // DG_PLAN: a measurement override of the planner's choice, "tile=BNxBM" and / or "splits=S"
 // (comma-separated; e.g. "tile=64x128,splits=4").  The tile must be one the planner could pick for
-// the form and size (64x64 or 64x128 for m <= 128; 256x128, 256x192 or 256x256 above, 256x128 for
-// the contiguous form); anything else is ignored.  Splits apply where the call may split K, as a
+// the form and size (64x64 or 64x128 for m <= 128; 256x128, 256x192 or 256x256 above, 256x128 or
+// 256x256 for the contiguous form, 256x128 for the row-scaled one); anything else is ignored.  Splits apply where the call may split K, as a
 // split of every tile.  Read at every call, like DG_DEBUG; the workspace queries see the same plan.
 static void apply_plan_override(Plan& pl, int layout, int64_t m, int kb_total, bool allow_split) {
   const char* e = std::getenv("DG_PLAN");
@@ -1125,8 +1171,9 @@ static void apply_plan_override(Plan& pl, int layout, int64_t m, int kb_total, b
     static const int kLargeCfgs[] = {kCfgRows128, kCfgWide, kCfgSquare};
     const bool few = layout != kContiguous && m <= 128;
     const int* list = few ? kDecCfgs : kLargeCfgs;
-    const int count = few ? 2 : (layout == kContiguous || layout == kDenseRowB ? 1 : 3);
+    const int count = few ? 2 : (layout == kDenseRowB ? 1 : 3);
     for (int i = 0; i < count; ++i) {
+      if (layout == kContiguous && list[i] == kCfgWide) continue;
       const LaunchInfo li = cfg_info<kDense>(list[i]);
       if (li.bn == bn && li.bm == bm) pl.cfg = layout == kDenseRowB && !few ? kCfgLarge : list[i];
     }
@@ -1139,23 +1186,25 @@ static void apply_plan_override(Plan& pl, int layout, int64_t m, int kb_total, b
   }
 }
 
-// Pick the tile config and the K split.  `groups` multiplies the tile count (masked layout).
+// Pick the tile config and the K split.  `groups`: the call's groups (masked: they multiply the
+// tile count; contiguous: the experts, which the tile choice weighs; otherwise 1).
 static Plan make_plan(int layout, int64_t m, int64_t n, int64_t k, int64_t groups, int num_cus, bool allow_split) {
   Plan pl = make_plan_auto(layout, m, n, k, groups, num_cus, allow_split);
   if (const char* e = std::getenv("DG_PLAN"); e != nullptr && e[0] != '\0') {
     apply_plan_override(pl, layout, m, (int)((k + kGroup - 1) / kGroup), allow_split);
-    finish_plan(pl, m, n, k, groups);
+    finish_plan(pl, m, n, k, layout == kMasked ? groups : 1);
   }
   return pl;
 }
 
 // The planner's own choice.
-static Plan make_plan_auto(int layout, int64_t m, int64_t n, int64_t k, int64_t groups, int num_cus,
+static Plan make_plan_auto(int layout, int64_t m, int64_t n, int64_t k, int64_t call_groups, int num_cus,
                            bool allow_split) {
+  const int64_t groups = layout == kMasked ? call_groups : 1;   // tiles per (m-block, n-block)
   if (layout != kContiguous && m <= 128) return make_decode_plan(m, n, k, groups, num_cus, allow_split);
   Plan pl{};
   const int kb_total = (int)((k + kGroup - 1) / kGroup);
-  pl.cfg = layout == kContiguous ? kCfgRows128
+  pl.cfg = layout == kContiguous ? choose_contiguous(m, n, call_groups, num_cus)
            : layout == kDenseRowB ? kCfgLarge
                                   : choose_large(m, n, groups, num_cus, kb_total, allow_split && layout == kDense);
   // (the 256x128 tile of the dense and masked forms is the pipelined one, kCfgRows128; kCfgLarge,
@@ -1189,7 +1238,8 @@ static Plan make_plan_auto(int layout, int64_t m, int64_t n, int64_t k, int64_t 
 
 void gemm_config_name(int layout, int64_t m, int64_t n, int64_t k, int64_t groups, int num_cus, char* buf,
                       size_t len) {
-  const Plan pl = make_plan(layout, m, n, k, layout == kMasked ? groups : 1, num_cus, layout != kContiguous);
+  const Plan pl = make_plan(layout, m, n, k, layout == kDense || layout == kDenseRowB ? 1 : groups, num_cus,
+                            layout != kContiguous);
   const LaunchInfo li = cfg_info<kDense>(pl.cfg);
   if (pl.tail_start > 0)   // whole tiles, then a split last round
     snprintf(buf, len, "%dx%d/%dwaves/split1+tail%d", li.bn, li.bm, li.threads / 64, pl.splits);
@@ -1267,10 +1317,10 @@ int launch_gemm(int layout, const uint8_t* a, const float* sa, int64_t ld_sa, co
     return set_error(kUnsupported, "gemm: one group's operand must be < 2^31 bytes (m=%lld n=%lld k=%lld ld=%lld)",
                      (long long)m, (long long)n, (long long)k, (long long)ld);
   if (layout == kMasked && groups > 1024) return set_error(kUnsupported, "masked gemm: at most 1024 groups");
-  const int64_t tile_groups = layout == kMasked ? groups : 1;
+  const int64_t plan_groups = layout == kDense || layout == kDenseRowB ? 1 : groups;
   const bool can_split = (layout != kContiguous) && ws != nullptr;
-  Plan pl = make_plan(layout, m, n, k, tile_groups, num_cus, can_split);
-  if (pl.splits > 1 && ws_bytes < pl.ws_bytes) pl = make_plan(layout, m, n, k, tile_groups, num_cus, false);
+  Plan pl = make_plan(layout, m, n, k, plan_groups, num_cus, can_split);
+  if (pl.splits > 1 && ws_bytes < pl.ws_bytes) pl = make_plan(layout, m, n, k, plan_groups, num_cus, false);
 
   GemmParams p = make_params(layout, pl, a, sa, ld_sa, b, sb, ld_sb, ld, d, m_indices, masked_m, groups, m, n, k);
   if (pl.splits > 1) {

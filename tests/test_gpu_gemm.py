@@ -439,3 +439,76 @@ def test_plan_override_results():
                 os.environ["DG_PLAN"] = old
         assert name.split("/")[0] == plan.split(",")[0][len("tile="):], name
         check_gemm(d, oracle.gemm.gemm_nt(qa, sa, qb, sb), f"forced {plan} {m}x{n}x{k}")
+
+
+# 128-row expert blocks of the two-pass contiguous cases: 256-row tiles (0,0) whole, (0,1), (-1,2),
+# (2,3) and (2,-1) split between two experts or an expert and an unmapped block, (-1,-1) unmapped,
+# and a last tile of one block.
+_TWO_PASS_BLOCKS = [0, 0, 0, 1, -1, 2, 2, 3, 2, -1, -1, -1, 3]
+
+
+@pytest.mark.parametrize("n,k", [(500, 1040), (512, 1040), (384, 128)])
+def test_contiguous_square_tiles(n, k):
+    """The contiguous form on 256x256 tiles (forced with DG_PLAN): tiles whose 128-row halves name
+    two experts run once per half and store only that half; unmapped halves and tiles are left
+    untouched; a tile of one block ends the rows.  N edges on both epilogue paths (N % 8 != 0 and
+    == 0), a partial last K group.  The same rows agree with the 256x128 plan bit for bit."""
+    import os
+    g = 4
+    m_idx = np.repeat(np.array(_TWO_PASS_BLOCKS, np.int32), 128)
+    m_total = m_idx.shape[0]
+    rng = inputs.rng_for("contig_square", n, k)
+    a = inputs.activations_with_outliers(rng, m_total, k)
+    b = inputs.grouped_weights(rng, g, n, k)
+    qa, sa = oracle.quant.quantize_per_token_group(a)
+    qb, sb = oracle.quant.quantize_per_block_grouped(b)
+    ref = oracle.gemm.gemm_grouped_contiguous(qa, sa, qb, sb, np.where(m_idx < 0, 0, m_idx))
+    mapped = m_idx >= 0
+    outs = {}
+    old = os.environ.get("DG_PLAN")
+    try:
+        for tile in ("256x256", "256x128"):
+            os.environ["DG_PLAN"] = "tile=" + tile
+            name = dg.dg_gemm_config_name(1, m_total, n, k, g)
+            say("gemm contiguous two-pass", m_total, n, k, name)
+            assert name.startswith(tile + "/"), name
+            d = torch.full((m_total, n), -1, dtype=torch.int16, device=device()).view(torch.bfloat16)
+            dg.dg_gemm_fp8_grouped_contiguous(to_dev(qa), sa_to_dev(sa), to_dev(qb), to_dev(sb), to_dev(m_idx), d=d)
+            torch.cuda.synchronize()
+            outs[tile] = d
+    finally:
+        if old is None:
+            os.environ.pop("DG_PLAN", None)
+        else:
+            os.environ["DG_PLAN"] = old
+    d = outs["256x256"]
+    bits = bf16_bits(d)
+    assert np.all(bits[~mapped] == BF16_NAN), "rows of unmapped blocks were written"
+    check_gemm(d[torch.from_numpy(mapped).to(device())], ref[mapped], f"contiguous 256x256 n={n} k={k}")
+    assert np.array_equal(bits, bf16_bits(outs["256x128"]))
+
+
+def test_contiguous_square_planner_choice():
+    """Large experts: the planner itself gives the contiguous form 256x256 tiles (under a CU cap
+    that makes them save rounds), one expert boundary inside a tile."""
+    g, n, k = 2, 1024, 256
+    m_idx = np.repeat(np.array([0] * 33 + [1] * 31, np.int32), 128)
+    m_total = m_idx.shape[0]
+    cap = _cap_for("256x256", 1, m_total, n, k, g)
+    assert cap is not None
+    rng = inputs.rng_for("contig_square_plan", n, k)
+    a = inputs.activations_with_outliers(rng, m_total, k)
+    b = inputs.grouped_weights(rng, g, n, k)
+    qa, sa = oracle.quant.quantize_per_token_group(a)
+    qb, sb = oracle.quant.quantize_per_block_grouped(b)
+    full = dg.dg_get_num_cus()
+    try:
+        dg.dg_set_num_cus(cap)
+        name = dg.dg_gemm_config_name(1, m_total, n, k, g)
+        say("gemm contiguous planner 256x256", m_total, n, k, "cap", cap, name)
+        d = dg.dg_gemm_fp8_grouped_contiguous(to_dev(qa), sa_to_dev(sa), to_dev(qb), to_dev(sb), to_dev(m_idx))
+        torch.cuda.synchronize()
+    finally:
+        dg.dg_set_num_cus(full)
+    assert name.startswith("256x256/"), name
+    check_gemm(d, oracle.gemm.gemm_grouped_contiguous(qa, sa, qb, sb, m_idx), "contiguous planner 256x256")

@@ -108,8 +108,8 @@ def test_plan_invariants_over_shapes():
                 assert splits == 1 and tail is None, name
             if layout == 3:   # per-row B scales run on the three-stage 256x128 tile only
                 assert (bn, bm) not in {(256, 192), (256, 256)}, name
-            if layout == 1:   # a contiguous tile spans one 128-row expert block
-                assert bm <= 128, name
+            if layout == 1:   # a contiguous tile spans one or two whole 128-row expert blocks
+                assert bm in (128, 256), name
             if layout == 0 and m <= 128:   # few rows: the 64-row weight tiles
                 assert bn == 64, (m, name)
             if layout in (0, 3) and m > 128:
@@ -135,8 +135,10 @@ def test_plan_override():
     assert got[(2, 128, 4096, 7168, 8)][0] == "64x128/4waves/split3"
     got = plans(cases, plan_override="tile=256x256")
     assert got[(0, 4096, 2112, 7168, 1)][0].startswith("256x256/8waves/")
-    assert got[(1, 4096, 2112, 7168, 4)][0].startswith("256x128/")   # contiguous: 256x128 only
+    assert got[(1, 4096, 2112, 7168, 4)][0].startswith("256x256/")
     assert got[(3, 4096, 2112, 7168, 1)][0].startswith("256x128/")   # row-scaled: 256x128 only
+    got = plans(cases, plan_override="tile=256x192")
+    assert got[(1, 4096, 2112, 7168, 4)] == base[(1, 4096, 2112, 7168, 4)]   # contiguous: no 192-row tile
     assert got[(0, 64, 2112, 7168, 1)] == base[(0, 64, 2112, 7168, 1)]   # not a few-row tile
     for junk in ("tile=100x7", "splits=0", "nonsense", "tile=64x64,splits=99"):
         got = plans(cases, plan_override=junk)
@@ -148,3 +150,16 @@ def test_plan_override():
                 pass
             else:
                 assert val == base[key], (junk, key, val)
+
+
+def test_contiguous_tile_choice():
+    """The contiguous form takes 256x256 tiles where its experts are large (few expert boundaries
+    per 256-row block, each costing one extra tile pass) and keeps 256x128 for many small experts:
+    the MoE workloads G = 4 and 8 with ~8192 rows per expert, and 64 Zipf-sized experts."""
+    cases = [[1, 31360, 4096, 7168, 4], [1, 31360, 7168, 2048, 4], [1, 62976, 4096, 7168, 8],
+             [1, 62976, 7168, 2048, 8], [1, 36608, 2048, 7168, 64], [1, 4096, 4096, 7168, 32]]
+    got = plans(cases)
+    for c in cases[:4]:
+        assert got[tuple(c)][0] == "256x256/8waves/split1", (c, got[tuple(c)])
+    for c in cases[4:]:
+        assert got[tuple(c)][0] == "256x128/8waves/split1", (c, got[tuple(c)])
