@@ -599,6 +599,9 @@ __global__ __launch_bounds__(C::kThreads) void gemm_fp8_kernel(GemmParams p) {
       static_assert(kBarRow >= 1, "PIPE: at least three fragment rows");
       constexpr uint32_t kOut = 0xFFFFFFF0u;   // an offset past every resource: the DMA writes zeros
       using SlotPtr = const uint8_t*;
+      // slot 0 (blocks 0, 2, ...) is the buffer the epilogue's strips do not use
+      uint8_t* const slot0 = st1;
+      uint8_t* const slot1 = st0;
       const int lane_off = lds_off(l16, 2 * g4);
       // this wave's activation-scale rows m0 + wm0 + lane (64 of them, the wave's WM first) and the
       // scale of its weight block, as byte offsets within a K block's scale row
@@ -618,7 +621,7 @@ __global__ __launch_bounds__(C::kThreads) void gemm_fp8_kernel(GemmParams p) {
       auto dma_ctx = [&](int tk, auto slot_c, bool valid) {
         constexpr int slot = decltype(slot_c)::value;
         DmaCtx c;
-        c.sbase = slot == 0 ? st0 : st1;
+        c.sbase = slot == 0 ? slot0 : slot1;
         c.kb = kb_begin + tk;
         c.base_off = dma_off;
         asm volatile("" : "+v"(c.base_off));
@@ -727,8 +730,8 @@ __global__ __launch_bounds__(C::kThreads) void gemm_fp8_kernel(GemmParams p) {
       auto bar_tail = [&](int tk, auto cur_c, auto nxt_c, v8i* a, v8i* bop, float* sc, float* rn) {
         constexpr int cur_slot = decltype(cur_c)::value;
         constexpr int nxt_slot = decltype(nxt_c)::value;
-        const SlotPtr cur = cur_slot == 0 ? st0 : st1;
-        const SlotPtr nxt = nxt_slot == 0 ? st0 : st1;
+        const SlotPtr cur = cur_slot == 0 ? slot0 : slot1;
+        const SlotPtr nxt = nxt_slot == 0 ? slot0 : slot1;
         __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0): this wave's reads of slot CUR are done
         wait_vmcnt<0>();                      // its DMAs of block tk+1 have landed
         __syncthreads();                      // ... and every wave's
@@ -739,33 +742,35 @@ __global__ __launch_bounds__(C::kThreads) void gemm_fp8_kernel(GemmParams p) {
         a[0] = n0a;
         a[1] = n1a;
       };
+      // Block 0's DMAs go out before the first wait, so that their latency overlaps the draining
+      // of the previous tile's output stores.  Every wave is past its last read of slot 0 (the
+      // previous tile's epilogue and K-split hand-off each begin with a barrier), and slot 1
+      // holds the epilogue's strips until the barrier below.
+      if (nk > 0) issue_pipe(0, IC<0>{}, true);   // (k = 0: no K block, the accumulators stay zero)
       wait_vmcnt<0>();
-      __syncthreads();   // the previous tile's readers are done with both slots
-      if (nk > 0) {      // (k = 0: no K block, the accumulators stay zero)
-      issue_pipe(0, IC<0>{}, true);
-      wait_vmcnt<0>();
-      __syncthreads();   // block 0 landed for every wave
+      __syncthreads();   // block 0 landed for every wave; every wave is done with the strips
+      if (nk > 0) {
       issue_pipe(1, IC<1>{}, nk > 1);
       v8i bop[kFM], a[3];
       float sc[kFM], r0[kFM + 1], r1[kFM + 1];
 #pragma unroll
-      for (int j = 0; j < kFM; ++j) bop[j] = read_b(st0, j);
-      read_scales(st0, r0);
-      a[0] = read_a(st0, 0);
-      a[1] = read_a(st0, 1);
+      for (int j = 0; j < kFM; ++j) bop[j] = read_b(slot0, j);
+      read_scales(slot0, r0);
+      a[0] = read_a(slot0, 0);
+      a[1] = read_a(slot0, 1);
       // block 0 up to its barrier row
-      rows(IC<0>{}, IC<kBarRow>{}, st0, st1, a, bop, sc, r0, nullptr);
+      rows(IC<0>{}, IC<kBarRow>{}, slot0, slot1, a, bop, sc, r0, nullptr);
       // two blocks per iteration (the slots alternate), while a block tk+2 follows; then the rest
       int tk = 0;
       for (; tk + 2 < nk; tk += 2) {
         bar_tail(tk, IC<0>{}, IC<1>{}, a, bop, sc, r1);
-        rows(IC<0>{}, IC<kBarRow>{}, st1, st0, a, bop, sc, r1, nullptr);
+        rows(IC<0>{}, IC<kBarRow>{}, slot1, slot0, a, bop, sc, r1, nullptr);
         bar_tail(tk + 1, IC<1>{}, IC<0>{}, a, bop, sc, r0);
-        rows(IC<0>{}, IC<kBarRow>{}, st0, st1, a, bop, sc, r0, nullptr);
+        rows(IC<0>{}, IC<kBarRow>{}, slot0, slot1, a, bop, sc, r0, nullptr);
       }
       bar_tail(tk, IC<0>{}, IC<1>{}, a, bop, sc, r1);
       if (tk + 1 < nk) {
-        rows(IC<0>{}, IC<kBarRow>{}, st1, st0, a, bop, sc, r1, nullptr);
+        rows(IC<0>{}, IC<kBarRow>{}, slot1, slot0, a, bop, sc, r1, nullptr);
         bar_tail(tk + 1, IC<1>{}, IC<0>{}, a, bop, sc, r0);
       }
       wait_vmcnt<0>();   // the zero-filling DMAs past the last K block
@@ -894,6 +899,7 @@ __global__ __launch_bounds__(C::kThreads) void gemm_fp8_kernel(GemmParams p) {
       continue;
     }
     const bool vec_ok = (p.n & 3) == 0;
+    __syncthreads();   // every wave is done with the ring (the next tile's first DMAs may follow at once)
 #pragma unroll
     for (int j = 0; j < C::kFragM; ++j) {
       const int mrow = m0 + wm0 + 16 * j + l16;
