@@ -24,7 +24,11 @@ Timing, two passes per workload:
     launches over R distinct copies of the weights (R copies > 768 MB, so no launch reads
     weights another left in the cache); duration = time / R, median over K steps.  This is
     the cold-weight duration a forward pass sees, and it amortises the event pair's own
-    few microseconds over R launches.  --no-flush / --no-rotate switch either off.
+    few microseconds over R launches.  --no-flush / --no-rotate switch either off.  A short
+    device spin (--spin-ms, 0.2 ms) opens each timing pass so the host's enqueue stays ahead;
+    a long one leaves the device nearly idle, and the MFMA-bound launches after it run slower
+    (16384 x 7168 x 16384: 1633 us after 0.2 ms, 1707 after 2 ms, 1873 after 20 ms), which a
+    loop of back-to-back kernels never sees.
 
 Prints ONE JSON line: the workload's GEMM FP8 TFLOP/s over the whole step, plus
 per-shape GEMM TFLOP/s and HBM GB/s, the roofline of the dominant GEMM kernel
@@ -79,8 +83,9 @@ def parse():
     ap.add_argument("--act-quant", default="separate", choices=["separate", "fused", "auto"],
                     help="dense workloads: activation quantization as its own launch (separate), inside the "
                          "GEMM launch (fused: dg_gemm_fp8_nt_act_quant), or inside it for M <= 128 only (auto)")
-    ap.add_argument("--spin-ms", type=float, default=20.0,
-                    help="device spin before each per-kernel timing pass (covers the host's enqueue time)")
+    ap.add_argument("--spin-ms", type=float, default=0.2,
+                    help="device spin before each per-kernel timing pass (gives the host's enqueue a head start; "
+                         "kept short: a long idle spin slows the MFMA-bound launches after it)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy (calibrates the FETCH_SIZE / WRITE_SIZE counters)")
     ap.add_argument("--plan-sweep", action="store_true",
@@ -775,8 +780,9 @@ def run_workload(name, args, torch, dg, dev, stream, flush_buf):
     # ---- per-launch durations, cold MALL.  A GEMM runs R times back to back over R copies of its
     # weights (R x weight bytes > 768 MB, so no launch finds its weights in the MALL) between one HIP
     # event pair on the stream, after an untimed 512 MB write; its duration is the pair's time / R.
-    # Other launches (quantizers) take one event pair each.  A bounded spin kernel at the start of
-    # every step keeps the device busy while the host enqueues it. -----------------------------------
+    # Other launches (quantizers) take one event pair each.  A short bounded spin kernel at the
+    # start of every step gives the host's enqueue a head start (a long one idles the device, and
+    # the MFMA-bound launches right after it run slower). -------------------------------------------
     for op in ops:
         if op.weights is not None and not args.no_rotate:
             wbytes = op.weights.numel() * op.weights.element_size()
