@@ -338,7 +338,9 @@ def test_cu_cap(cap):
     with the cap); a capped call whose plan equals the uncapped one is bit-identical to it."""
     say("gemm cu cap", cap)
     full = dg.dg_get_num_cus()
-    cases = [(64, 512, 4096), (300, 1000, 1024), (128, 256, 2048)]
+    # (520, 1003, 1024): large tiles with the direct-store epilogue (N % 8 != 0), several per
+    # workgroup under the small caps
+    cases = [(64, 512, 4096), (300, 1000, 1024), (128, 256, 2048), (520, 1003, 1024)]
     try:
         for (m, n, k) in cases:
             qa, sa, qb, sb = quantized_operands("cucap", m, n, k)
@@ -447,12 +449,14 @@ def test_plan_override_results():
 _TWO_PASS_BLOCKS = [0, 0, 0, 1, -1, 2, 2, 3, 2, -1, -1, -1, 3]
 
 
-@pytest.mark.parametrize("n,k", [(500, 1040), (512, 1040), (384, 128)])
-def test_contiguous_square_tiles(n, k):
+@pytest.mark.parametrize("n,k,cap", [(500, 1040, None), (512, 1040, None), (384, 128, None), (500, 1040, 3),
+                                     (512, 1040, 2)])
+def test_contiguous_square_tiles(n, k, cap):
     """The contiguous form on 256x256 tiles (forced with DG_PLAN): tiles whose 128-row halves name
     two experts run once per half and store only that half; unmapped halves and tiles are left
     untouched; a tile of one block ends the rows.  N edges on both epilogue paths (N % 8 != 0 and
-    == 0), a partial last K group.  The same rows agree with the 256x128 plan bit for bit."""
+    == 0), a partial last K group; with a CU cap, one workgroup runs several tiles and passes in
+    a row.  The same rows agree with the 256x128 plan bit for bit."""
     import os
     g = 4
     m_idx = np.repeat(np.array(_TWO_PASS_BLOCKS, np.int32), 128)
@@ -466,17 +470,21 @@ def test_contiguous_square_tiles(n, k):
     mapped = m_idx >= 0
     outs = {}
     old = os.environ.get("DG_PLAN")
+    full = dg.dg_get_num_cus()
     try:
+        if cap is not None:
+            dg.dg_set_num_cus(cap)
         for tile in ("256x256", "256x128"):
             os.environ["DG_PLAN"] = "tile=" + tile
             name = dg.dg_gemm_config_name(1, m_total, n, k, g)
-            say("gemm contiguous two-pass", m_total, n, k, name)
+            say("gemm contiguous two-pass", m_total, n, k, name, "cap", cap)
             assert name.startswith(tile + "/"), name
             d = torch.full((m_total, n), -1, dtype=torch.int16, device=device()).view(torch.bfloat16)
             dg.dg_gemm_fp8_grouped_contiguous(to_dev(qa), sa_to_dev(sa), to_dev(qb), to_dev(sb), to_dev(m_idx), d=d)
             torch.cuda.synchronize()
             outs[tile] = d
     finally:
+        dg.dg_set_num_cus(full)
         if old is None:
             os.environ.pop("DG_PLAN", None)
         else:
