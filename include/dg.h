@@ -358,7 +358,8 @@ const char* dg_gemm_config_name(int layout, int64_t m, int64_t n, int64_t k, int
  * Planner override for measurement (DG_PLAN, read at every call): "tile=BNxBM" and / or
  * "splits=S", comma-separated (e.g. "tile=64x128,splits=4").  The tile replaces the planner's
  * choice when it is one the planner could pick for the form and size (64x64 or 64x128 for
- * m <= 128 rows; 256x128, 256x192 or 256x256 above; 256x128 for the contiguous form); splits
+ * m <= 128 rows; 256x128, 256x192 or 256x256 above; 256x128 or 256x256 for the contiguous form,
+ * 256x128 for the row-scaled one); splits
  * (1..16) split every tile's K range where the call may split K.  Anything else is ignored.
  * dg_gemm_config_name and dg_gemm_workspace_size report the overridden plan; results stay within
  * the GEMM tolerance (a different K split changes the fp32 summation order).  For measuring the
