@@ -124,7 +124,26 @@ class Op:
 
 def dense_gemm_bytes(m, n, k):
     """Algorithmic HBM bytes of one dense GEMM: A + its scales, B + its scales, bf16 D."""
-    return m * k + 4 * m * (k // 128) + n * k + 4 * (-(-n // 128)) * (k // 128) + 2 * m * n
+    kb = -(-k // 128)
+    return m * k + 4 * m * kb + n * k + 4 * (-(-n // 128)) * kb + 2 * m * n
+
+
+def contiguous_gemm_bytes(m_total, n, k, groups):
+    """Algorithmic HBM bytes of one contiguous-grouped GEMM: the padded rows of A + their scales,
+    every expert's B + its scales, the padded rows of bf16 D, and the int32 expert index per row."""
+    kb = -(-k // 128)
+    return (m_total * k + 4 * m_total * kb + groups * (n * k + 4 * (-(-n // 128)) * kb)
+            + 2 * m_total * n + 4 * m_total)
+
+
+def masked_gemm_bytes(masked_m, m_max, n, k):
+    """Algorithmic HBM bytes of one masked-grouped GEMM: B + its scales of every expert with rows,
+    each valid row's A (k bytes), its scales (k/32 bytes) and its bf16 D row, and the counts."""
+    masked_m = np.asarray(masked_m)
+    rows = int(np.sum(np.clip(masked_m, 0, m_max)))
+    active = int(np.sum(masked_m > 0))
+    kb = -(-k // 128)
+    return active * (n * k + 4 * (-(-n // 128)) * kb) + rows * (k + 4 * kb + 2 * n) + 4 * len(masked_m)
 
 
 def quant_bytes(elems, k, in_bytes=4):
@@ -277,8 +296,7 @@ def build_contiguous(torch, dg, dev, cases):
         ops.append(Op("aquant", f"aq {m_total}x{k}",
                       (lambda a32=a32, qa=qa, sa=sa: dg.dg_quantize_per_token_group(a32, q=qa, sa=sa)),
                       nbytes=quant_bytes(m_total * k, k)))
-        nbytes = (m_total * k + 4 * m_total * (k // 128) + g * (n * k + 4 * (-(-n // 128)) * (k // 128))
-                  + 2 * m_total * n + 4 * m_total)
+        nbytes = contiguous_gemm_bytes(m_total, n, k, g)
         make = (lambda w, qa=qa, sa=sa, sb=sb, m_idx=m_idx, d=d:
                 dg.dg_gemm_fp8_grouped_contiguous(qa, sa, w, sb, m_idx, d=d))
         ops.append(Op("gemm", f"{label} G={g} rows={rows} (padded {m_total}) N={n} K={k}",
@@ -375,14 +393,13 @@ def build_masked(torch, dg, dev, cases):
         masked = torch.from_numpy(masked_np.astype(np.int32)).to(dev)
         ws = dg.default_workspace(dev, dg.dg_gemm_workspace_size(m_max, n, k, g))
         rows = int(np.sum(np.clip(masked_np, 0, m_max)))
-        active = int(np.sum(masked_np > 0))
         ops.append(Op("wquant", f"wq {g}x{n}x{k}",
                       (lambda w32=w32, qb=qb, sb=sb: dg.dg_quantize_per_block(w32, q=qb, sb=sb)),
                       nbytes=quant_bytes(g * n * k, k)))
         ops.append(Op("aquant", f"aq {g}x{m_max}x{k}",
                       (lambda a32=a32, qa=qa, sa=sa: dg.dg_quantize_per_token_group(a32, q=qa, sa=sa)),
                       nbytes=quant_bytes(g * m_max * k, k)))
-        nbytes = active * (n * k + 4 * (-(-n // 128)) * (k // 128)) + rows * (k + k // 32 + 2 * n) + 4 * g
+        nbytes = masked_gemm_bytes(masked_np, m_max, n, k)
         make = (lambda w, qa=qa, sa=sa, sb=sb, d=d, masked=masked, ws=ws:
                 dg.dg_gemm_fp8_grouped_masked(qa, sa, w, sb, masked, d=d, workspace=ws))
         ops.append(Op("gemm", f"masked G={g} rows={rows} M_max={m_max} N={n} K={k}",
