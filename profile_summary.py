@@ -56,17 +56,44 @@ def gemm_config(name):
             f"{' +act-quant' if m.group(7) == 'true' else ''}")
 
 
+def is_flush(name, us):
+    """bench.py's untimed 512 MB write ahead of every timed GEMM group (a byte fill of ~100 us)."""
+    return "FillFunctor" in name and us >= 20.0
+
+
 def cmd_trace(args):
     per = defaultdict(list)
+    disp = []
     with open(args.csv) as fh:
         for r in csv.DictReader(fh):
-            per[short_name(r["Kernel_Name"])].append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+            us = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
+            per[short_name(r["Kernel_Name"])].append(us)
+            disp.append((int(r["Start_Timestamp"]), r["Kernel_Name"], us))
+    # the per-launch pass: GEMM dispatches that follow a flush with only GEMM dispatches between
+    # (bench.py's R launches over rotated weights); the rest are the step's warm-up and graph replays
+    per_launch = defaultdict(list)
+    after_flush = False
+    for _, name, us in sorted(disp):
+        if is_flush(name, us):
+            after_flush = True
+        elif _CFG.search(name):
+            if after_flush:
+                per_launch[short_name(name)].append(us)
+        else:
+            after_flush = False
     rows = sorted(per.items(), key=lambda kv: -sum(kv[1]))
     total = sum(sum(v) for v in per.values())
     lines = [f"# rocprofv3 kernel trace: {args.title}", "", "Command:", "", "```", args.command, "```", "",
              "| kernel | dispatches | avg us | total us | share |", "|---|---|---|---|---|"]
     for k, v in rows:
         lines.append(f"| {k} | {len(v)} | {sum(v) / len(v):.2f} | {sum(v):.1f} | {100 * sum(v) / total:.1f}% |")
+    if per_launch:
+        lines += ["", "GEMM dispatches of bench.py's per-launch pass only (those right after its 512 MB flush: "
+                  "the launches its per-launch durations and roofline time; the table above also holds the "
+                  "step's warm-up and graph-replay dispatches):", "",
+                  "| kernel | dispatches | avg us |", "|---|---|---|"]
+        for k, v in sorted(per_launch.items(), key=lambda kv: -sum(kv[1])):
+            lines.append(f"| {k} | {len(v)} | {sum(v) / len(v):.2f} |")
     os.makedirs(os.path.dirname(os.path.abspath(args.out)), exist_ok=True)
     with open(args.out, "w") as fh:
         fh.write("\n".join(lines) + "\n")
