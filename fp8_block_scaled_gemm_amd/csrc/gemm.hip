@@ -960,9 +960,13 @@ static LaunchInfo info() {
 //              least time in rounds of the persistent grid (wave quantisation decides most shapes).
 //              In the contiguous form a tile spans two 128-row expert blocks and runs once per
 //              expert when they differ.
-//  kCfgDec*    m <= 128 rows: 64 weight rows x 64 or 128 activation rows, 4 waves, two
-//              workgroups per CU: HBM-bound shapes (for 65..128 rows the planner's model picks
-//              one 128-row or two 64-row activation tiles).  (Measured against 128-row weight
+//  kCfgDec*    m <= 128 rows: 64 weight rows x 64 or 128 activation rows, 4 waves, a two-stage
+//              ring: HBM-bound shapes (for 65..128 rows the planner's model picks one 128-row or
+//              two 64-row activation tiles).  Each barrier waits for every DMA in flight, so a
+//              workgroup has one stage in flight whatever the ring's depth; two stages leave LDS
+//              for four (64x64) or three (64x128) workgroups per CU, against two with the
+//              four- and three-stage rings (the twelve M = 64 / 128 DeepSeek-V3 shapes 5% faster
+//              at their best plans).  (Measured against 128-row weight
 //              tiles on all twelve M = 64 / 128 DeepSeek-V3 shapes: the 64-row weight tile, with
 //              K split to fill the grid, is faster on every one.)
 enum CfgId : int { kCfgLarge = 0, kCfgRows128, kCfgWide, kCfgDec64, kCfgDec128, kCfgSquare, kNumCfg };
@@ -970,8 +974,8 @@ using CfgLarge = Cfg<256, 128, 64, 64, 3, true>;
 using CfgRows128 = Cfg<256, 128, 64, 64, 2, false, true>;
 using CfgWide = Cfg<256, 192, 128, 48, 2, false, true>;
 using CfgSquare = Cfg<256, 256, 128, 64, 2, false, true>;
-using CfgDec64 = Cfg<64, 64, 32, 32, 4>;
-using CfgDec128 = Cfg<64, 128, 32, 64, 3>;
+using CfgDec64 = Cfg<64, 64, 32, 32, 2>;
+using CfgDec128 = Cfg<64, 128, 32, 64, 2>;
 
 template <int LAYOUT, bool FQ = false>
 static LaunchInfo cfg_info(int cfg) {
@@ -1096,13 +1100,13 @@ static int choose_contiguous(int64_t m, int64_t n, int64_t experts, int num_cus)
   return t_square < t_rows ? kCfgSquare : kCfgRows128;
 }
 
-// Few-row plan (m <= 128 rows per group): the K split from a model of the streaming regime, fitted to
-// timings of every split on MI355X.  Work items spread evenly over the CUs; a CU running c
-// workgroups keeps c * (STAGES - 1) stages of both operand tiles in flight, each taking ~1.5 us
-// to arrive; the whole grid is further bound by HBM (~5 TB/s for the weights, read once) and by
-// L2-to-CU delivery (~8 TB/s for both tiles: the activation tile is re-read by every weight
-// tile); a split's hand-off costs ~2 us plus the last workgroup's read of every partial at
-// ~100 GB/s.  Returns the estimated time in microseconds.
+// Few-row plan (m <= 128 rows per group): the tile and K split from a model of the streaming regime,
+// fitted to timings of every tile and split on MI355X.  Work items spread evenly over the CUs; a
+// workgroup has one stage in flight per K block (the barrier waits for every DMA in flight) and
+// takes ~0.6 us per K block, and a CU runs c of them side by side; the whole grid is further bound
+// by HBM (~5 TB/s for the weights, read once) and by L2-to-CU delivery (both tiles: the activation
+// tile is re-read by every weight tile); a split's hand-off costs ~2 us plus the last workgroup's
+// read of every partial at ~50 GB/s.  Returns the estimated time in microseconds.
 static double decode_estimate(const LaunchInfo& li, int occ, int64_t m, int64_t n, int kb_total, int64_t groups,
                               int num_cus, int splits, int kbps) {
   const int64_t tiles = ((m + li.bm - 1) / li.bm) * ((n + li.bn - 1) / li.bn) * groups;
@@ -1110,13 +1114,12 @@ static double decode_estimate(const LaunchInfo& li, int occ, int64_t m, int64_t 
   const int64_t per_cu = (items + num_cus - 1) / num_cus;
   const double conc = (double)(per_cu < occ ? per_cu : occ);
   const double stage = (double)(li.bn + li.bm) * kGroup;
-  const double rate = conc * (li.stages - 1) * stage / 1.5;   // bytes per us
-  double t = (double)per_cu * stage * kbps / rate;
-  const double l2 = (double)items * stage * kbps / 8.0e6;
+  double t = (double)per_cu * kbps * 0.6 / conc;
+  const double l2 = (double)items * stage * kbps / 16.0e6;
   const double hbm = (double)tiles * li.bn * kGroup * kb_total / 5.0e6;
   if (t < l2) t = l2;
   if (t < hbm) t = hbm;
-  if (splits > 1) t += 2.0 + (double)splits * li.bn * li.bm * 4 / 1.0e5;
+  if (splits > 1) t += 2.0 + (double)splits * li.bn * li.bm * 4 / 5.0e4;
   return t;
 }
 

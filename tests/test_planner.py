@@ -51,10 +51,10 @@ NAME = re.compile(r"^(\d+)x(\d+)/(\d+)waves/split(\d+)(?:\+tail(\d+))?$")
 V3_PLANS = {
     (64, 2112, 7168): "64x64/4waves/split8", (64, 24576, 1536): "64x64/4waves/split1",
     (64, 32768, 512): "64x64/4waves/split1", (64, 7168, 16384): "64x64/4waves/split4",
-    (64, 4096, 7168): "64x64/4waves/split4", (64, 7168, 2048): "64x64/4waves/split4",
-    (128, 2112, 7168): "64x64/4waves/split4", (128, 24576, 1536): "64x128/4waves/split1",
+    (64, 4096, 7168): "64x64/4waves/split6", (64, 7168, 2048): "64x64/4waves/split4",
+    (128, 2112, 7168): "64x64/4waves/split6", (128, 24576, 1536): "64x128/4waves/split1",
     (128, 32768, 512): "64x128/4waves/split1", (128, 7168, 16384): "64x128/4waves/split4",
-    (128, 4096, 7168): "64x128/4waves/split4", (128, 7168, 2048): "64x64/4waves/split1",
+    (128, 4096, 7168): "64x128/4waves/split6", (128, 7168, 2048): "64x128/4waves/split4",
     (4096, 2112, 7168): "256x192/8waves/split1", (4096, 24576, 1536): "256x256/8waves/split1",
     (4096, 32768, 512): "256x256/8waves/split1", (4096, 7168, 16384): "256x256/8waves/split1",
     (4096, 4096, 7168): "256x256/8waves/split1", (4096, 7168, 2048): "256x256/8waves/split1",
